@@ -1,0 +1,11 @@
+"""CPU oracle for exact softmax attention over a paged KV cache (test infrastructure).
+
+This package is the ground truth that the HIP path is checked against. Only tests/,
+__graft_entry__.smoke() and bench.py's cpu_baseline leg may import it; the library and its
+Python binding never do. It shares no code with the HIP path.
+"""
+from .naive_attention import (attention, attend_rows, gather_kv, visible_keys,
+                              softmax_weights, flops_visible_pairs)
+
+__all__ = ["attention", "attend_rows", "gather_kv", "visible_keys", "softmax_weights",
+           "flops_visible_pairs"]
