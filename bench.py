@@ -1,0 +1,241 @@
+"""Benchmark of the exact paged attention path on one MI355X.
+
+One step is one pass of the whole path over one batch of the mixed long-context workload
+(120 decode requests with contexts in [4096, 32768] plus 8 prefill requests of 2048 query
+tokens, 64 q / 8 kv heads, head_size 128, bf16, block_size 64, a 2048-token prefix shared by
+all requests), through both of its layer passes (pass 0 causal, pass 1 causal with a
+4096-token sliding window), each with its own q and KV cache. Per pass the batch is sent to
+the library as its decode rows (split-KV kernel + LSE merge) and its prefill rows (prefill
+kernel), on one stream, with HIP events between the calls so that the kernels' durations are
+measured inside the timed region.
+
+Prints one JSON line. ``value`` is the fraction of the MI355X roofline reached by the whole
+step, in percent: (prefill flops / 2.5 PFLOP/s + decode bytes / 8 TB/s) / step time, where
+flops and bytes are algorithmic (visible (query, key) pairs only; K/V bytes each request must
+read, the shared prefix counted once per layer). ``roofline`` describes the dominant kernel
+(prefill, bf16 MFMA). ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12      # MI355X HBM3E
+METRIC = "prefill attn TFLOP/s + decode KV GB/s at 1 MI355X, % of roofline"
+
+
+def algorithmic_work(batch, causal, window):
+    """(prefill flops, decode unique bytes, decode logical bytes) of one layer pass.
+
+    Prefill flops: 4 * head_size per visible (query, key) pair and q head. Decode bytes: the
+    K and V rows of every visible key of every kv head, plus q, out, lse and the block-table
+    entries of the visible blocks. 'logical' counts each request's keys; 'unique' counts the
+    shared-prefix keys once (the prefix is the same physical blocks for every request)."""
+    import oracle  # only for the visible-pair count of the definition
+    nd = batch.num_decodes
+    d, hq, hkv = batch.head_size, batch.num_heads, batch.num_kv_heads
+    pairs = oracle.flops_visible_pairs(batch.query_lens[nd:], batch.seq_lens[nd:], causal, window)
+    prefill_flops = 4.0 * d * hq * pairs
+    row = 2 * hkv * d * 2                                   # K + V bytes of one token
+    S = batch.shared_prefix_blocks * batch.block_size
+    shared_seen = np.zeros(S, dtype=bool)
+    logical_tok = private_tok = bt_entries = 0
+    for r in range(nd):
+        sl = int(batch.seq_lens[r])
+        lo = max(0, sl - window) if window > 0 else 0
+        logical_tok += sl - lo
+        private_tok += sl - max(lo, S)
+        if lo < S:
+            shared_seen[lo:min(sl, S)] = True
+        bt_entries += -(-sl // batch.block_size) - lo // batch.block_size
+    extra = nd * (hq * d * 2 * 2 + hq * 4) + bt_entries * 4   # q + out (bf16), lse, table
+    unique = (private_tok + int(shared_seen.sum())) * row + extra
+    logical = logical_tok * row + extra
+    return prefill_flops, unique, logical
+
+
+def cpu_baseline(batch, layers, seed):
+    """Time the oracle on a bounded sample: every 10th decode request and 4 query rows of each
+    prefill request, for every layer pass; scale to the metric's unit (percent of the MI355X
+    roofline the CPU reaches on that sample)."""
+    import torch
+    import gen
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    nd = batch.num_decodes
+    dec = list(range(0, nd, 10))
+    pre = list(range(nd, batch.num_seqs))
+    floor_s = 0.0
+    cpu_s = 0.0
+    for li, (q, kv) in enumerate(layers):
+        causal, window = batch.passes[li]
+        sub, qs, kvs = gen.subset(batch, dec + pre, q, kv)
+        qsl = sub.query_start_loc
+        rows = list(range(len(dec)))
+        for i in range(len(dec), sub.num_seqs):
+            ql = int(sub.query_lens[i])
+            rows += [int(qsl[i]) + x for x in np.linspace(0, ql - 1, 4).astype(int)]
+        qn = qs.to(torch.float32).numpy()
+        kvn = kvs.to(torch.float32).numpy()
+        t0 = time.perf_counter()
+        oracle.attention(qn, kvn, sub.block_table, qsl, sub.seq_lens, sub.scale, causal, window,
+                         rows=rows)
+        cpu_s += time.perf_counter() - t0
+        # roofline floor of the sampled work on the GPU
+        d, hq = sub.head_size, sub.num_heads
+        flops = 0.0
+        for i in range(len(dec), sub.num_seqs):
+            ql, sl = int(sub.query_lens[i]), int(sub.seq_lens[i])
+            pos = (sl - ql) + np.linspace(0, ql - 1, 4).astype(int)
+            lo = np.maximum(pos - window + 1, 0) if window > 0 else 0
+            flops += 4.0 * d * hq * float(np.sum(pos + 1 - lo))
+        byts = 0.0
+        for i in range(len(dec)):
+            sl = int(sub.seq_lens[i])
+            lo = max(0, sl - window) if window > 0 else 0
+            byts += (sl - lo) * 2 * sub.num_kv_heads * d * 2
+        floor_s += flops / PEAK_BF16_FLOPS + byts / PEAK_HBM_BYTES
+    return {"value": 100.0 * floor_s / cpu_s, "unit": "% of MI355X roofline", "cores": threads,
+            "kind": "oracle", "seconds": round(cpu_s, 3),
+            "sample": f"fp64 numpy oracle; per layer pass: decode requests {dec[0]}..{dec[-1]} "
+                      f"step 10 ({len(dec)} of {nd}) and 4 evenly spaced query rows of each of "
+                      f"the {len(pre)} prefill requests, all 64 q heads; value = GPU-roofline "
+                      f"time of that work / CPU time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_softmax_attention_paged_amd as A
+    import gen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    batch = gen.config(5, seed=args.seed)
+    nd = batch.num_decodes
+    tok0 = int(batch.query_start_loc[nd])
+
+    layers = [gen.make_tensors(batch, args.seed, dev, layer=li) for li in range(len(batch.passes))]
+    bt = torch.from_numpy(batch.block_table).to(dev)
+    sl = torch.from_numpy(batch.seq_lens).to(dev)
+    qsl_np = batch.query_start_loc
+    qsl_dec = torch.from_numpy(qsl_np[:nd + 1].copy()).to(dev)
+    qsl_pre = torch.from_numpy((qsl_np[nd:] - qsl_np[nd]).astype(np.int32)).to(dev)
+    bt_dec, bt_pre = bt[:nd].contiguous(), bt[nd:].contiguous()
+    sl_dec, sl_pre = sl[:nd].contiguous(), sl[nd:].contiguous()
+    common = dict(num_heads=batch.num_heads, num_kv_heads=batch.num_kv_heads,
+                  head_size=batch.head_size, num_blocks=batch.num_blocks,
+                  block_size=batch.block_size, max_blocks_per_seq=batch.max_blocks_per_seq,
+                  dtype=A.ATTN_BF16)
+    desc_dec = A.make_desc(num_seqs=nd, num_tokens=nd, num_decodes=nd, max_query_len=1,
+                           max_seq_len=int(batch.seq_lens[:nd].max()), **common)
+    desc_pre = A.make_desc(num_seqs=batch.num_seqs - nd, num_tokens=batch.num_tokens - tok0,
+                           num_decodes=0, max_query_len=int(batch.query_lens[nd:].max()),
+                           max_seq_len=int(batch.seq_lens[nd:].max()), **common)
+    ws = torch.empty(A.attn_workspace_bytes(desc_dec), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(q) for q, _ in layers]
+    lses = [torch.empty(batch.num_tokens, batch.num_heads, dtype=torch.float32, device=dev)
+            for _ in layers]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        for li, (q, kv) in enumerate(layers):
+            causal, window = batch.passes[li]
+            if ev is not None:
+                ev[li][0].record(stream)
+            A.attn_varlen_fwd(desc_dec, q[:nd], kv, bt_dec, qsl_dec, sl_dec, batch.scale,
+                              causal, window, outs[li][:nd], lses[li][:nd], ws, stream)
+            if ev is not None:
+                ev[li][1].record(stream)
+            A.attn_varlen_fwd(desc_pre, q[tok0:], kv, bt_pre, qsl_pre, sl_pre, batch.scale,
+                              causal, window, outs[li][tok0:], lses[li][tok0:], None, stream)
+            if ev is not None:
+                ev[li][2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers]
+           for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = 1e3 * wall / args.steps
+
+    dec_ms = np.mean([sum(e[li][0].elapsed_time(e[li][1]) for li in range(len(layers)))
+                      for e in evs])
+    pre_ms_per_launch = np.mean([e[li][1].elapsed_time(e[li][2]) for e in evs
+                                 for li in range(len(layers))])
+    pre_ms = pre_ms_per_launch * len(layers)
+    flops = dbytes_u = dbytes_l = 0.0
+    per_pass = []
+    for (causal, window) in batch.passes:
+        f, bu, bl = algorithmic_work(batch, causal, window)
+        per_pass.append({"causal": causal, "window": window, "prefill_gflop": f / 1e9,
+                         "decode_gb_unique": bu / 1e9, "decode_gb_logical": bl / 1e9})
+        flops += f
+        dbytes_u += bu
+        dbytes_l += bl
+    floor_s = flops / PEAK_BF16_FLOPS + dbytes_u / PEAK_HBM_BYTES
+    value = 100.0 * floor_s / (ms_step / 1e3)
+    achieved = (flops / len(layers)) / (pre_ms_per_launch / 1e3) / 1e12
+    rec = {
+        "metric": METRIC, "value": round(value, 3), "unit": "% of roofline",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "mixed-long-context: 120 decode (ctx U[4096,32768]) + 8 prefill "
+                               "(q 2048, ctx U[4096,32768]), 64 q / 8 kv heads, d 128, bf16, "
+                               "block 64, 2048-token shared prefix, 2 layer passes "
+                               "(causal; causal + window 4096)",
+                   "global_batch": batch.num_seqs, "num_tokens": batch.num_tokens,
+                   "seed": args.seed, "parallelism": "none (1 GPU)"},
+        "prefill_tflops": round(flops / (pre_ms / 1e3) / 1e12, 2),
+        "decode_gbps": round(dbytes_u / (dec_ms / 1e3) / 1e9, 1),
+        "decode_gbps_logical": round(dbytes_l / (dec_ms / 1e3) / 1e9, 1),
+        "prefill_ms_per_step": round(pre_ms, 4), "decode_ms_per_step": round(dec_ms, 4),
+        "per_pass": per_pass,
+        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128,causal>",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_FLOPS / 1e12,
+                     "unit": "TFLOP/s", "frac": round(achieved / (PEAK_BF16_FLOPS / 1e12), 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(batch, layers, args.seed)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

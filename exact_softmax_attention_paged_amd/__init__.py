@@ -1,0 +1,178 @@
+"""Python binding of libattn.so: exact softmax attention over a paged KV cache on gfx950.
+
+The functions here carry the names of the C entry points declared in include/attn.h and do
+argument marshalling only: they check that tensors have the dtype, device and contiguity the
+C ABI expects, pass their data pointers and the current HIP stream, and turn status codes into
+exceptions. Every step of the attention itself runs in the library's HIP kernels. PyTorch only
+provides device memory and streams. If the library has not been built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_BLOCK_SIZE, ATTN_ERR_GQA = 0, 1, 2, 3, 4
+ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_METADATA, ATTN_ERR_HIP = 5, 6, 7, 8
+ATTN_BF16, ATTN_F32 = 0, 1
+
+EXPORTED = ("attn_workspace_bytes", "attn_varlen_fwd", "attn_check_metadata_host",
+            "attn_status_str")
+
+
+class attn_desc(ctypes.Structure):
+    """Mirror of struct attn_desc in include/attn.h (13 x int32)."""
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_seqs", "num_tokens", "num_decodes", "max_query_len", "max_seq_len", "num_heads",
+        "num_kv_heads", "head_size", "num_blocks", "block_size", "max_blocks_per_seq", "dtype",
+        "partition_tokens")]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {attn_status_str(status)} ({status})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library. torch is imported first so that the process holds one HIP runtime."""
+    global _lib
+    if _lib is None:
+        import torch  # noqa: F401  (loads the HIP runtime that torch uses)
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m exact_softmax_attention_paged_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        P = ctypes.POINTER
+        L.attn_workspace_bytes.argtypes = [P(attn_desc), P(sz)]
+        L.attn_workspace_bytes.restype = i32
+        L.attn_varlen_fwd.argtypes = [P(attn_desc), vp, vp, vp, vp, vp, f32, i32, i32, vp, vp,
+                                      vp, sz, vp]
+        L.attn_varlen_fwd.restype = i32
+        L.attn_check_metadata_host.argtypes = [P(attn_desc), vp, vp, vp]
+        L.attn_check_metadata_host.restype = i32
+        L.attn_status_str.argtypes = [i32]
+        L.attn_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def attn_status_str(status: int) -> str:
+    return lib().attn_status_str(int(status)).decode()
+
+
+def make_desc(*, num_seqs, num_tokens, num_decodes, max_query_len, max_seq_len, num_heads,
+              num_kv_heads, head_size, num_blocks, block_size, max_blocks_per_seq, dtype,
+              partition_tokens=0) -> attn_desc:
+    return attn_desc(int(num_seqs), int(num_tokens), int(num_decodes), int(max_query_len),
+                     int(max_seq_len), int(num_heads), int(num_kv_heads), int(head_size),
+                     int(num_blocks), int(block_size), int(max_blocks_per_seq), int(dtype),
+                     int(partition_tokens))
+
+
+def attn_workspace_bytes(desc: attn_desc) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().attn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_workspace_bytes")
+    return int(n.value)
+
+
+def attn_check_metadata_host(desc: attn_desc, block_table: np.ndarray,
+                             query_start_loc: np.ndarray, seq_lens: np.ndarray) -> int:
+    """Returns the status code (ATTN_OK or ATTN_ERR_METADATA, ...); host arrays only."""
+    arrs = [np.ascontiguousarray(a, dtype=np.int32) for a in (block_table, query_start_loc,
+                                                               seq_lens)]
+    ptrs = [a.ctypes.data_as(ctypes.c_void_p) for a in arrs]
+    return int(lib().attn_check_metadata_host(ctypes.byref(desc), *ptrs))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_tensor(name, t, dtype, device, allow_none=False):
+    if t is None:
+        if allow_none:
+            return
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def attn_varlen_fwd(desc: attn_desc, q, kv_cache, block_table, query_start_loc, seq_lens,
+                    scale: float, causal: bool, window: int, out, lse, workspace,
+                    stream=None) -> None:
+    """Queue the attention of one varlen batch on ``stream`` (default: torch's current stream).
+
+    Tensors follow include/attn.h: q/out [num_tokens, Hq, d], kv_cache
+    [2, num_blocks, block_size, Hkv, d] (bf16 or f32 as desc.dtype), int32 metadata, fp32 lse
+    (or None) and a uint8 workspace of attn_workspace_bytes(desc) bytes (or None if 0)."""
+    import torch
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("attn_varlen_fwd runs on a GPU device; q is on " + str(dev))
+    dt = torch.bfloat16 if desc.dtype == ATTN_BF16 else torch.float32
+    _check_tensor("q", q, dt, dev)
+    _check_tensor("kv_cache", kv_cache, dt, dev)
+    _check_tensor("out", out, dt, dev)
+    for n, t in (("block_table", block_table), ("query_start_loc", query_start_loc),
+                 ("seq_lens", seq_lens)):
+        _check_tensor(n, t, torch.int32, dev)
+    _check_tensor("lse", lse, torch.float32, dev, allow_none=True)
+    if workspace is not None:
+        _check_tensor("workspace", workspace, torch.uint8, dev)
+    if tuple(q.shape) != (desc.num_tokens, desc.num_heads, desc.head_size) or \
+            tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q/out shape does not match desc")
+    if tuple(kv_cache.shape) != (2, desc.num_blocks, desc.block_size, desc.num_kv_heads,
+                                 desc.head_size):
+        raise ValueError("kv_cache shape does not match desc")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib().attn_varlen_fwd(ctypes.byref(desc), _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                               _ptr(query_start_loc), _ptr(seq_lens), float(scale),
+                               1 if causal else 0, int(window), _ptr(out), _ptr(lse),
+                               _ptr(workspace), ws_bytes, ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_varlen_fwd")
+
+
+def varlen_fwd(q, kv_cache, block_table, query_start_loc, seq_lens, *, scale, causal, window=0,
+               num_decodes, max_query_len, max_seq_len, partition_tokens=0, out=None,
+               lse=None, want_lse=True, workspace=None):
+    """Convenience wrapper: builds the descriptor from tensor shapes plus the host scalars,
+    allocates out / lse / workspace with torch when not given, and calls attn_varlen_fwd.
+    Returns (out, lse)."""
+    import torch
+    dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_F32
+    desc = make_desc(num_seqs=seq_lens.numel(), num_tokens=q.shape[0], num_decodes=num_decodes,
+                     max_query_len=max_query_len, max_seq_len=max_seq_len,
+                     num_heads=q.shape[1], num_kv_heads=kv_cache.shape[3],
+                     head_size=q.shape[2], num_blocks=kv_cache.shape[1],
+                     block_size=kv_cache.shape[2], max_blocks_per_seq=block_table.shape[1],
+                     dtype=dtype, partition_tokens=partition_tokens)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = attn_workspace_bytes(desc)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    attn_varlen_fwd(desc, q, kv_cache, block_table, query_start_loc, seq_lens, scale, causal,
+                    window, out, lse, workspace)
+    return out, lse

@@ -1,0 +1,195 @@
+// C-ABI layer of libattn.so: argument validation, workspace sizing, the decode/prefill
+// dispatch from host scalars, and the launches on the caller's stream. See include/attn.h.
+#include "attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int32_t kDefaultPartition = 512;
+
+int32_t partition_tokens(const attn_desc* d) {
+  return d->partition_tokens > 0 ? d->partition_tokens : kDefaultPartition;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Checks that need nothing but the descriptor.
+attn_status check_desc(const attn_desc* d) {
+  if (d == nullptr) return ATTN_ERR_NULL;
+  if (d->num_seqs < 0 || d->num_tokens < 0 || d->num_decodes < 0 || d->max_query_len < 0 ||
+      d->max_seq_len < 0 || d->num_heads <= 0 || d->num_kv_heads <= 0 || d->num_blocks < 0 ||
+      d->max_blocks_per_seq < 0 || d->num_decodes > d->num_seqs ||
+      d->max_query_len > d->max_seq_len)
+    return ATTN_ERR_SHAPE;
+  if (d->block_size <= 0 || d->block_size % 16 != 0) return ATTN_ERR_BLOCK_SIZE;
+  if (d->num_heads % d->num_kv_heads != 0) return ATTN_ERR_GQA;
+  if (d->head_size != 64 && d->head_size != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d->dtype != ATTN_BF16 && d->dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (d->partition_tokens < 0 || (d->partition_tokens > 0 && d->partition_tokens % 128 != 0))
+    return ATTN_ERR_UNSUPPORTED;
+  if (d->num_seqs > 65535) return ATTN_ERR_SHAPE;                    // grid z limit
+  if ((int64_t)d->max_seq_len > (int64_t)d->max_blocks_per_seq * d->block_size)
+    return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+bool uses_split_decode(const attn_desc* d) { return d->dtype == ATTN_BF16 && d->num_decodes > 0; }
+
+// Partitions a decode request may span: all of max_seq_len, or with a window at most
+// ceil(window / P) + 1 of them.
+int64_t decode_max_parts(const attn_desc* d, int32_t window) {
+  const int64_t P = partition_tokens(d);
+  int64_t n = ceil_div(d->max_seq_len, P);
+  if (window > 0) {
+    const int64_t wn = ceil_div(window, P) + 1;
+    if (wn < n) n = wn;
+  }
+  return n < 1 ? 1 : n;
+}
+
+size_t workspace_for(const attn_desc* d, int64_t max_parts) {
+  if (!uses_split_decode(d)) return 0;
+  const int64_t rows = (int64_t)d->num_decodes * d->num_heads * max_parts;
+  const int64_t floats = rows * d->head_size + rows;
+  return (size_t)ceil_div(floats * 4, 256) * 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_workspace_bytes(const attn_desc* desc, size_t* bytes) {
+  if (bytes == nullptr) return ATTN_ERR_NULL;
+  const attn_status s = check_desc(desc);
+  if (s != ATTN_OK) return s;
+  *bytes = workspace_for(desc, decode_max_parts(desc, 0));
+  return ATTN_OK;
+}
+
+attn_status attn_varlen_fwd(const attn_desc* desc, const void* q, const void* kv_cache,
+                            const int32_t* block_table, const int32_t* query_start_loc,
+                            const int32_t* seq_lens, float scale, int32_t causal,
+                            int32_t window, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  attn_status s = check_desc(desc);
+  if (s != ATTN_OK) return s;
+  const attn_desc& d = *desc;
+  if (window > 0 && !causal) return ATTN_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (d.num_seqs == 0 || d.num_tokens == 0) return ATTN_OK;
+  if (q == nullptr || kv_cache == nullptr || block_table == nullptr ||
+      query_start_loc == nullptr || seq_lens == nullptr || out == nullptr)
+    return ATTN_ERR_NULL;
+
+  const int64_t max_parts = decode_max_parts(&d, window);
+  const size_t need = workspace_for(&d, max_parts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t v_offset = (int64_t)d.num_blocks * d.block_size * d.num_kv_heads * d.head_size;
+
+  attn::PrefillParams pp{};
+  pp.q = q;
+  pp.kv = kv_cache;
+  pp.block_table = block_table;
+  pp.qsl = query_start_loc;
+  pp.seq_lens = seq_lens;
+  pp.out = out;
+  pp.lse = lse;
+  pp.v_offset = v_offset;
+  pp.num_heads = d.num_heads;
+  pp.num_kv_heads = d.num_kv_heads;
+  pp.head_size = d.head_size;
+  pp.block_size = d.block_size;
+  pp.max_blocks = d.max_blocks_per_seq;
+  pp.max_query_len = d.max_query_len;
+  pp.causal = causal ? 1 : 0;
+  pp.window = window > 0 ? window : 0;
+  pp.scale = scale;
+
+  if (d.dtype == ATTN_F32) {
+    // float32 runs every request, decode rows included, through the fp32 prefill kernel
+    pp.seq_begin = 0;
+    pp.num_seqs = d.num_seqs;
+    return attn::launch_prefill_f32(pp, st) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  }
+
+  if (d.num_decodes > 0) {
+    attn::DecodeParams dp{};
+    dp.q = q;
+    dp.kv = kv_cache;
+    dp.block_table = block_table;
+    dp.qsl = query_start_loc;
+    dp.seq_lens = seq_lens;
+    dp.out = out;
+    dp.lse = lse;
+    dp.ws_o = static_cast<float*>(workspace);
+    dp.ws_lse = static_cast<float*>(workspace) +
+                (int64_t)d.num_decodes * d.num_heads * max_parts * d.head_size;
+    dp.v_offset = v_offset;
+    dp.num_heads = d.num_heads;
+    dp.num_kv_heads = d.num_kv_heads;
+    dp.head_size = d.head_size;
+    dp.block_size = d.block_size;
+    dp.max_blocks = d.max_blocks_per_seq;
+    dp.num_decodes = d.num_decodes;
+    dp.part_tokens = partition_tokens(&d);
+    dp.max_parts = (int32_t)max_parts;
+    dp.window = pp.window;
+    dp.scale = scale;
+    if (attn::launch_decode_bf16(dp, st) != hipSuccess) return ATTN_ERR_HIP;
+  }
+  if (d.num_seqs > d.num_decodes) {
+    pp.seq_begin = d.num_decodes;
+    pp.num_seqs = d.num_seqs - d.num_decodes;
+    if (attn::launch_prefill_bf16(pp, st) != hipSuccess) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+attn_status attn_check_metadata_host(const attn_desc* desc, const int32_t* block_table,
+                                     const int32_t* query_start_loc, const int32_t* seq_lens) {
+  const attn_status s = check_desc(desc);
+  if (s != ATTN_OK) return s;
+  const attn_desc& d = *desc;
+  if (d.num_seqs == 0) return d.num_tokens == 0 ? ATTN_OK : ATTN_ERR_METADATA;
+  if (block_table == nullptr || query_start_loc == nullptr || seq_lens == nullptr)
+    return ATTN_ERR_NULL;
+  if (query_start_loc[0] != 0 || query_start_loc[d.num_seqs] != d.num_tokens)
+    return ATTN_ERR_METADATA;
+  for (int32_t r = 0; r < d.num_seqs; ++r) {
+    const int64_t ql = (int64_t)query_start_loc[r + 1] - query_start_loc[r];
+    const int64_t sl = seq_lens[r];
+    if (ql < 0 || sl < ql || sl > d.max_seq_len || ql > d.max_query_len) return ATTN_ERR_METADATA;
+    if (r < d.num_decodes && ql != 1) return ATTN_ERR_METADATA;
+    const int64_t nb = ceil_div(sl, d.block_size);
+    if (nb > d.max_blocks_per_seq) return ATTN_ERR_METADATA;
+    for (int64_t b = 0; b < nb; ++b) {
+      const int32_t blk = block_table[(int64_t)r * d.max_blocks_per_seq + b];
+      if (blk < 0 || blk >= d.num_blocks) return ATTN_ERR_METADATA;
+    }
+  }
+  return ATTN_OK;
+}
+
+const char* attn_status_str(int32_t status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_NULL: return "ATTN_ERR_NULL";
+    case ATTN_ERR_SHAPE: return "ATTN_ERR_SHAPE";
+    case ATTN_ERR_BLOCK_SIZE: return "ATTN_ERR_BLOCK_SIZE";
+    case ATTN_ERR_GQA: return "ATTN_ERR_GQA";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+    case ATTN_ERR_METADATA: return "ATTN_ERR_METADATA";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+    default: return "ATTN_ERR_UNKNOWN";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,316 @@
+// Split-KV decode attention (query_len == 1) and the log-sum-exp merge, bf16, for gfx950.
+//
+// Method: the RBLN "Attention 모드" page (Overview, Flash Attention bullet) processes each
+// request's KV cache partition by partition and combines the per-partition results with online
+// softmax. Here one workgroup handles one (decode request, kv head, partition of
+// part_tokens keys) and all q heads that share that kv head (num_queries_per_kv of the vLLM
+// FlashAttention page's FlashAttentionImpl section), so every K/V byte is read from HBM once
+// per kv head. The partition result (normalised output and its lse) goes to the workspace,
+// and a second kernel merges the partitions of each (request, q head) through their
+// log-sum-exp. A request whose visible keys fit one partition is written directly.
+//
+// Inside a workgroup each of the 4 waves streams its own quarter of the partition in 32-key
+// chunks, with the next chunk's loads issued before the current chunk's math:
+//   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: K rows go straight from HBM into the A
+//     operand (16-byte loads), the q heads of the group sit in the 16 MFMA columns;
+//   * V rows are copied into a wave-private LDS tile and read back transposed with
+//     ds_read_b64_tr_b16 as the A operand of O^T += V^T . P^T;
+//   * the 4 waves' (max, sum, O) are combined through LDS at the end.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kChunk = 32;       // keys per wave iteration
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams p) {
+  constexpr int RS = D + 16;           // LDS row stride (bf16) of a V chunk
+  constexpr int KC = D / 32;
+  constexpr int DC = D / 16;
+  constexpr int TPR = D / 8;           // lanes per V row in the copy
+  constexpr int RPI = kWave / TPR;     // V rows per copy instruction
+  constexpr int NV = kChunk / RPI;     // copy instructions per chunk
+  constexpr int V_TILE = kChunk * RS;  // bf16 per wave tile
+  constexpr int OS = D + 4;            // fp32 row stride of the combine buffer
+
+  // V tiles during the stream; reused as the combine buffer afterwards
+  constexpr int kLdsBytes = (kWaves * V_TILE * 2 > kWaves * 16 * OS * 4)
+                                ? kWaves * V_TILE * 2 : kWaves * 16 * OS * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  __shared__ float sM[kWaves][16];
+  __shared__ float sL[kWaves][16];
+
+  const int r = blockIdx.z;
+  const int group = p.num_heads / p.num_kv_heads;
+  const int head_groups = (group + 15) / 16;
+  const int kvh = blockIdx.y / head_groups;
+  const int hg = blockIdx.y % head_groups;
+  const int nh = min(16, group - hg * 16);             // q heads in this workgroup
+  const int h0 = kvh * group + hg * 16;                // first q head
+
+  const int sl = p.seq_lens[r];
+  int first, nparts;
+  decode_partitions(sl, p.window, p.part_tokens, &first, &nparts);
+  nparts = min(nparts, p.max_parts);   // only reachable with seq_len > max_seq_len
+  const int pi = blockIdx.x;
+  if (pi >= nparts) return;
+  const int part = first + pi;
+  const int lo = p.window > 0 ? max(0, sl - p.window) : 0;
+  const int k_begin = max(lo, part * p.part_tokens);
+  const int k_end = min(sl, (part + 1) * p.part_tokens);
+  const int tok = p.qsl[r];
+
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int lane = tid % kWave;
+  const int G = lane / 16;
+  const int li = lane % 16;
+
+  const __bf16* __restrict__ q = static_cast<const __bf16*>(p.q);
+  const __bf16* __restrict__ kcache = static_cast<const __bf16*>(p.kv);
+  const __bf16* __restrict__ vcache = kcache + p.v_offset;
+  const int32_t* __restrict__ bt = p.block_table + (int64_t)r * p.max_blocks;
+
+  // Q^T (B operand): lane (G, li) holds q head h0 + li, d = 32c + 8G .. +7
+  bf16x8 qf[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    qf[c] = li < nh ? *reinterpret_cast<const bf16x8*>(
+                          q + ((int64_t)tok * p.num_heads + h0 + li) * D + 32 * c + 8 * G)
+                    : bf16x8{};
+  }
+
+  // this wave's key range: quarter w of the partition, clipped to the visible range
+  const int quarter = p.part_tokens / kWaves;
+  const int w_begin = max(k_begin, part * p.part_tokens + w * quarter);
+  const int w_end = min(k_end, part * p.part_tokens + (w + 1) * quarter);
+  // chunks are aligned to the quarter start (a multiple of 32), so a 16-key MFMA tile never
+  // straddles a block (block_size is a multiple of 16)
+  const int c_base = part * p.part_tokens + w * quarter;
+  const int c_first = w_end > w_begin ? (w_begin - c_base) / kChunk : 0;
+  const int n_chunks =
+      w_end > w_begin ? (w_end - (c_base + c_first * kChunk) + kChunk - 1) / kChunk : 0;
+
+  __bf16* sVw = reinterpret_cast<__bf16*>(lds) + w * V_TILE;
+  const int v_row = lane / TPR;
+  const int v_chunk = lane % TPR;
+
+  u32x4 kreg[2][KC], vreg[NV];
+  auto load_chunk = [&](int kb) {
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int key = kb + 16 * t2 + li;
+      if (key < sl) {
+        const int32_t blk = bt[key / p.block_size];
+        const int64_t off = paged_row(blk, key % p.block_size, kvh, p.block_size,
+                                      p.num_kv_heads, D) + 8 * G;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) kreg[t2][c] = *reinterpret_cast<const u32x4*>(kcache + off + 32 * c);
+      } else {
+#pragma unroll
+        for (int c = 0; c < KC; ++c) kreg[t2][c] = u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int key = kb + j * RPI + v_row;
+      if (key < sl) {
+        const int32_t blk = bt[key / p.block_size];
+        const int64_t off = paged_row(blk, key % p.block_size, kvh, p.block_size,
+                                      p.num_kv_heads, D) + 8 * v_chunk;
+        vreg[j] = *reinterpret_cast<const u32x4*>(vcache + off);
+      } else {
+        vreg[j] = u32x4{0, 0, 0, 0};   // past seq_len: zero so that 0 * V stays 0
+      }
+    }
+  };
+
+  const float c_log2 = p.scale * kLog2e;
+  float m_run = -INFINITY, l_run = 0.f;
+  floatx4 o[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) o[dc] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (n_chunks > 0) load_chunk(c_base + c_first * kChunk);
+  for (int ci = 0; ci < n_chunks; ++ci) {
+    const int kb = c_base + (c_first + ci) * kChunk;
+    // V chunk -> wave-private LDS tile (row-major [key][d])
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      *reinterpret_cast<u32x4*>(&sVw[(j * RPI + v_row) * RS + 8 * v_chunk]) = vreg[j];
+    bf16x8 kf[2][KC];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) kf[t2][c] = __builtin_bit_cast(bf16x8, kreg[t2][c]);
+    if (ci + 1 < n_chunks) load_chunk(kb + kChunk);
+
+    floatx4 sc[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) acc = mfma16x16x32(kf[t2][c], qf[c], acc);
+      sc[t2] = acc;
+    }
+    if (kb < w_begin || kb + kChunk > w_end) {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = kb + 16 * t2 + 4 * G + e;
+          if (j < w_begin || j >= w_end) sc[t2][e] = -INFINITY;
+        }
+    }
+
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = column_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2((m_run - m_use) * c_log2);
+    const float mc = m_use * c_log2;
+    float lsum = 0.f;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pv = fast_exp2(fmaf(sc[t2][e], c_log2, -mc));
+        sc[t2][e] = pv;
+        lsum += pv;
+      }
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+    const bf16x8 pb = pack_bf16x8(sc[0], sc[1]);
+
+    // the LDS writes above must land before other lanes of this wave read them
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int r0 = 4 * G + li / 4;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const int col = 16 * dc + 4 * (li % 4);
+      const bf16x8 va = concat(lds_read_tr16(&sVw[r0 * RS + col]),
+                               lds_read_tr16(&sVw[(r0 + 16) * RS + col]));
+      o[dc] = mfma16x16x32(va, pb, o[dc] * alpha);
+    }
+    // the next chunk's LDS writes must not pass these reads
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+
+  // ---- combine the 4 waves: (m, l, O^T) -> partition result
+  const float l_w = column_sum(l_run);
+  __syncthreads();   // every wave is done with its V tile; the LDS becomes the combine buffer
+  float* sO = reinterpret_cast<float*>(lds);
+  if (G == 0) {
+    sM[w][li] = m_run;
+    sL[w][li] = l_w;
+  }
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc)
+    *reinterpret_cast<floatx4*>(&sO[(w * 16 + li) * OS + 16 * dc + 4 * G]) = o[dc];
+  __syncthreads();
+
+  constexpr int DPT = D / 16;          // d values per thread: 256 threads = 16 heads x 16
+  const int hh = tid / 16;             // head within the workgroup
+  const int d0 = (tid % 16) * DPT;
+  if (hh >= nh) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sM[ww][hh]);
+  const float M_use = (M == -INFINITY) ? 0.f : M;
+  float wgt[kWaves];
+  float L = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < kWaves; ++ww) {
+    wgt[ww] = fast_exp2((sM[ww][hh] - M_use) * c_log2);
+    L += sL[ww][hh] * wgt[ww];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float acc[DPT];
+#pragma unroll
+  for (int x = 0; x < DPT; ++x) {
+    float a = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) a += wgt[ww] * sO[(ww * 16 + hh) * OS + d0 + x];
+    acc[x] = a * inv;
+  }
+  const float lse_part = L > 0.f ? p.scale * M + __logf(L) : -INFINITY;
+  const int hq = h0 + hh;
+  if (nparts == 1) {
+    __bf16* dst = static_cast<__bf16*>(p.out) + ((int64_t)tok * p.num_heads + hq) * D + d0;
+#pragma unroll
+    for (int x = 0; x < DPT; ++x) dst[x] = to_bf16(acc[x]);
+    if (p.lse != nullptr && d0 == 0) p.lse[(int64_t)tok * p.num_heads + hq] = lse_part;
+  } else {
+    const int64_t slot = ((int64_t)r * p.num_heads + hq) * p.max_parts + pi;
+    float* dst = p.ws_o + slot * D + d0;
+#pragma unroll
+    for (int x = 0; x < DPT; x += 4)
+      *reinterpret_cast<floatx4*>(dst + x) = floatx4{acc[x], acc[x + 1], acc[x + 2], acc[x + 3]};
+    if (d0 == 0) p.ws_lse[slot] = lse_part;
+  }
+}
+
+// One wave per (q head, decode request): out = sum_p exp(lse_p - L) o_p, lse = L.
+template <int D>
+__global__ __launch_bounds__(64) void lse_merge_kernel(const DecodeParams p) {
+  const int hq = blockIdx.x;
+  const int r = blockIdx.y;
+  const int sl = p.seq_lens[r];
+  int first, nparts;
+  decode_partitions(sl, p.window, p.part_tokens, &first, &nparts);
+  nparts = min(nparts, p.max_parts);
+  if (nparts <= 1) return;        // written directly by the split kernel
+  const int lane = threadIdx.x;
+  const int64_t base = ((int64_t)r * p.num_heads + hq) * p.max_parts;
+  float M = -INFINITY;
+  for (int pi = lane; pi < nparts; pi += kWave) M = fmaxf(M, p.ws_lse[base + pi]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float M_use = (M == -INFINITY) ? 0.f : M;
+  float S = 0.f;
+  for (int pi = lane; pi < nparts; pi += kWave) S += fast_exp2((p.ws_lse[base + pi] - M_use) * kLog2e);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
+  const float L = S > 0.f ? M_use + __logf(S) : -INFINITY;
+  constexpr int DPL = D / kWave;
+  float acc[DPL];
+#pragma unroll
+  for (int x = 0; x < DPL; ++x) acc[x] = 0.f;
+  for (int pi = 0; pi < nparts; ++pi) {
+    const float wgt = S > 0.f ? fast_exp2((p.ws_lse[base + pi] - L) * kLog2e) : 0.f;
+    const float* src = p.ws_o + (base + pi) * D;
+#pragma unroll
+    for (int x = 0; x < DPL; ++x) acc[x] += wgt * src[lane + kWave * x];
+  }
+  const int tok = p.qsl[r];
+  __bf16* dst = static_cast<__bf16*>(p.out) + ((int64_t)tok * p.num_heads + hq) * D;
+#pragma unroll
+  for (int x = 0; x < DPL; ++x) dst[lane + kWave * x] = to_bf16(acc[x]);
+  if (p.lse != nullptr && lane == 0) p.lse[(int64_t)tok * p.num_heads + hq] = L;
+}
+
+template <int D>
+hipError_t launch(const DecodeParams& p, hipStream_t stream) {
+  const int group = p.num_heads / p.num_kv_heads;
+  const int head_groups = (group + 15) / 16;
+  const dim3 grid(p.max_parts, p.num_kv_heads * head_groups, p.num_decodes);
+  hipLaunchKernelGGL(decode_split_kernel<D>, grid, dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.max_parts <= 1) return e;
+  hipLaunchKernelGGL(lse_merge_kernel<D>, dim3(p.num_heads, p.num_decodes), dim3(kWave), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
+  if (p.num_decodes <= 0) return hipSuccess;
+  return p.head_size == 64 ? launch<64>(p, stream) : launch<128>(p, stream);
+}
+
+}  // namespace attn

@@ -1,0 +1,57 @@
+// Launch interface between the C-ABI layer and the gfx950 kernels (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// One prefill launch covers requests [seq_begin, seq_begin + num_seqs) and every q head.
+struct PrefillParams {
+  const void* q;                // [num_tokens][num_heads][head_size]
+  const void* kv;               // (2, num_blocks, block_size, num_kv_heads, head_size)
+  const int32_t* block_table;   // [num_seqs_total][max_blocks]
+  const int32_t* qsl;           // [num_seqs_total + 1]
+  const int32_t* seq_lens;      // [num_seqs_total]
+  void* out;
+  float* lse;                   // may be null
+  int64_t v_offset;             // elements between the K half and the V half
+  int32_t num_heads, num_kv_heads, head_size, block_size, max_blocks;
+  int32_t seq_begin, num_seqs, max_query_len;
+  int32_t causal, window;
+  float scale;
+};
+
+// One split-KV decode launch covers requests [0, num_decodes): each has query_len == 1.
+struct DecodeParams {
+  const void* q;
+  const void* kv;
+  const int32_t* block_table;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  void* out;
+  float* lse;
+  float* ws_o;                  // [num_decodes][num_heads][max_parts][head_size]
+  float* ws_lse;                // [num_decodes][num_heads][max_parts]
+  int64_t v_offset;
+  int32_t num_heads, num_kv_heads, head_size, block_size, max_blocks;
+  int32_t num_decodes, part_tokens, max_parts;  // max_parts: partitions a request may span
+  int32_t window;
+  float scale;
+};
+
+// Partitions of a decode request that hold visible keys: [first, first + count).
+__host__ __device__ inline void decode_partitions(int32_t seq_len, int32_t window,
+                                                  int32_t part_tokens, int32_t* first,
+                                                  int32_t* count) {
+  int32_t lo = window > 0 ? (seq_len - window > 0 ? seq_len - window : 0) : 0;
+  int32_t f = lo / part_tokens;
+  int32_t end = (seq_len + part_tokens - 1) / part_tokens;
+  *first = f;
+  *count = end > f ? end - f : 0;
+}
+
+hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,162 @@
+/*
+ * attn.h — C ABI of the MI355X (gfx950) exact paged attention library, libattn.so.
+ *
+ * The library computes exact scaled-dot-product attention over a paged KV cache for a
+ * variable-length batch in one call, FlashAttention-style: scores are formed tile by tile,
+ * the softmax is kept online (running max and running sum), partial results over KV
+ * partitions are merged through their log-sum-exp, and the N x N score matrix never reaches
+ * device memory.
+ *
+ * Sources (web pages this library follows; cited by title and section):
+ *   [FA]   "[vLLM] FlashAttention: IO-aware 타일링으로 어텐션 연산을 가속하는 원리"
+ *            - FlashAttentionBackend section: cache shape (2, num_blocks, block_size,
+ *              num_kv_heads, head_size) and the block_size % 16 rule;
+ *            - FlashAttentionImpl section: scale, num_kv_heads, num_queries_per_kv (GQA);
+ *            - FlashAttentionMetadata section: query_start_loc, seq_lens, block_table,
+ *              max_query_len, max_seq_len, one kernel call per varlen batch;
+ *            - Intro and paper-summary sections: tiling plus online softmax, exactness.
+ *   [RBLN] "Attention 모드" (RBLN vLLM docs): Overview (naive attention; partitions merged
+ *              by online softmax), Full Attention (causal), Sliding-Window Attention.
+ *   [OTH]  "[vLLM] 기타 Attention Backends ...", Triton Attention section:
+ *              seq_len = context_len + query_len.
+ *   [LIN]  "[vLLM] Lightning & Linear Attention ...", Prefill/Decode split section:
+ *              requests with query_len == 1 are decode requests.
+ *
+ * Conventions for every entry point:
+ *   - All tensors are caller-owned. Device pointers must stay valid until the work queued
+ *     on `stream` has finished. The library never allocates, frees or synchronises device
+ *     memory and keeps no global state; calls are thread-safe.
+ *   - Errors are reported as attn_status codes. Argument errors are detected on the host
+ *     before anything is queued, so a failed call leaves every buffer untouched.
+ *   - Device-side metadata (block_table, query_start_loc, seq_lens) is trusted by
+ *     attn_varlen_fwd: checking it would need a device-to-host synchronisation.
+ *     attn_check_metadata_host validates host copies of it.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* a size is negative or sizes are inconsistent */
+  ATTN_ERR_BLOCK_SIZE = 3,  /* block_size is not a positive multiple of 16 ([FA] Backend) */
+  ATTN_ERR_GQA = 4,         /* num_heads is not a multiple of num_kv_heads ([FA] Impl) */
+  ATTN_ERR_UNSUPPORTED = 5, /* head_size, dtype, partition size or mask kind not built */
+  ATTN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than attn_workspace_bytes */
+  ATTN_ERR_METADATA = 7,    /* attn_check_metadata_host found malformed metadata */
+  ATTN_ERR_HIP = 8          /* a kernel launch failed */
+} attn_status;
+
+typedef enum attn_dtype {
+  ATTN_BF16 = 0, /* q, kv_cache and out are bfloat16; accumulation is fp32 */
+  ATTN_F32 = 1   /* q, kv_cache and out are float32 */
+} attn_dtype;
+
+/*
+ * Host-side scalars describing one call. They mirror the scalar fields of the
+ * FlashAttentionMetadata section of [FA] (num_actual_tokens, max_query_len, max_seq_len)
+ * plus the per-layer constants of its FlashAttentionImpl section. Passing them from the
+ * host keeps the call free of device-to-host synchronisation.
+ */
+typedef struct attn_desc {
+  int32_t num_seqs;           /* requests in the batch */
+  int32_t num_tokens;         /* query rows = query_start_loc[num_seqs] */
+  int32_t num_decodes;        /* requests [0, num_decodes) have query_len == 1 ([LIN]) and
+                                 take the split-KV decode path; 0 sends every request
+                                 through the prefill kernel */
+  int32_t max_query_len;      /* >= every query_len */
+  int32_t max_seq_len;        /* >= every seq_len */
+  int32_t num_heads;          /* query heads Hq */
+  int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0; q head h reads kv head h / (Hq/Hkv) */
+  int32_t head_size;          /* d: 64 or 128 */
+  int32_t num_blocks;         /* physical blocks in kv_cache */
+  int32_t block_size;         /* tokens per block, a positive multiple of 16 */
+  int32_t max_blocks_per_seq; /* row stride of block_table */
+  int32_t dtype;              /* attn_dtype */
+  int32_t partition_tokens;   /* split-KV partition length for decode rows: 0 means 512;
+                                 otherwise a positive multiple of 128 */
+} attn_desc;
+
+/*
+ * attn_workspace_bytes: device workspace that attn_varlen_fwd needs for `desc`.
+ * It holds the per-partition partial outputs and log-sum-exps of the decode rows
+ * ([RBLN] Overview: partition results combined by online softmax):
+ *   num_decodes * num_heads * P * (head_size + 1) * 4 bytes, rounded up to 256,
+ * where P is the number of partitions of max_seq_len (capped for a window in
+ * attn_varlen_fwd). Returns 0 bytes when num_decodes == 0 or dtype is ATTN_F32.
+ * Errors: ATTN_ERR_NULL (desc or bytes NULL), and the same shape checks as attn_varlen_fwd
+ * that do not depend on the window.
+ */
+attn_status attn_workspace_bytes(const attn_desc* desc, size_t* bytes);
+
+/*
+ * attn_varlen_fwd: exact attention for a variable-length batch over a paged KV cache.
+ *
+ * For request r, let q0 = query_start_loc[r], ql = query_start_loc[r+1] - q0,
+ * sl = seq_lens[r] and cl = sl - ql ([OTH] Triton section). Query row i (0 <= i < ql) sits at
+ * absolute position p = cl + i. For every q head h, with kv head kh = h / (Hq/Hkv), it attends
+ * to keys j in [0, sl) with j <= p when `causal` ([RBLN] Full Attention) and j >= p - window + 1
+ * when window > 0 ([RBLN] SWA); key j is K/V row
+ *   kv_cache[0 or 1][block_table[r * max_blocks_per_seq + j / block_size]][j % block_size][kh]
+ * ([FA] Backend). With s_j = scale * q . k_j:
+ *   out[q0+i][h] = sum_j softmax(s)_j v_j,   lse[q0+i][h] = ln sum_j exp(s_j).
+ * A row with no visible key gets out = 0 and lse = -inf.
+ *
+ * Arguments (device pointers unless noted):
+ *   desc            host pointer, see attn_desc.
+ *   q               [num_tokens][num_heads][head_size], dtype of desc, rows packed by request.
+ *   kv_cache        [2][num_blocks][block_size][num_kv_heads][head_size], dtype of desc.
+ *                   Slots past seq_len and unused blocks are never read into the result.
+ *   block_table     int32 [num_seqs][max_blocks_per_seq]; entries past a request's last
+ *                   block are never read.
+ *   query_start_loc int32 [num_seqs + 1], non-decreasing, query_start_loc[0] = 0.
+ *   seq_lens        int32 [num_seqs], seq_len >= query_len.
+ *   scale           softmax scale applied to q . k ([FA] Impl).
+ *   causal          nonzero for causal masking (bottom-right aligned as above).
+ *   window          > 0: sliding window of `window` keys including the query's own position;
+ *                   requires causal. <= 0: no window.
+ *   out             [num_tokens][num_heads][head_size], dtype of desc; every row is written.
+ *   lse             float32 [num_tokens][num_heads], or NULL to skip it.
+ *   workspace       device scratch of at least attn_workspace_bytes(desc) bytes (may be NULL
+ *                   when that is 0); its contents on entry do not matter.
+ *   workspace_bytes size of workspace.
+ *   stream          hipStream_t to queue on (NULL = the null stream). The call returns as
+ *                   soon as the kernels are queued.
+ *
+ * Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_BLOCK_SIZE ([FA] Backend raises on
+ * block_size % 16 != 0), ATTN_ERR_GQA, ATTN_ERR_UNSUPPORTED (head_size not 64/128, unknown
+ * dtype, partition_tokens not a multiple of 128, window > 0 without causal),
+ * ATTN_ERR_WORKSPACE, ATTN_ERR_HIP (launch failure).
+ */
+attn_status attn_varlen_fwd(const attn_desc* desc, const void* q, const void* kv_cache,
+                            const int32_t* block_table, const int32_t* query_start_loc,
+                            const int32_t* seq_lens, float scale, int32_t causal,
+                            int32_t window, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * attn_check_metadata_host: validates host copies of the metadata against desc:
+ * query_start_loc starts at 0, is non-decreasing and ends at num_tokens; 0 <= query_len <=
+ * seq_len <= max_seq_len; query_len <= max_query_len; requests [0, num_decodes) have
+ * query_len == 1; ceil(seq_len / block_size) <= max_blocks_per_seq; every block id a request
+ * uses lies in [0, num_blocks). All pointers are host pointers; nothing touches the GPU.
+ * Returns ATTN_OK, ATTN_ERR_METADATA, or the desc errors of attn_varlen_fwd.
+ */
+attn_status attn_check_metadata_host(const attn_desc* desc, const int32_t* block_table,
+                                     const int32_t* query_start_loc, const int32_t* seq_lens);
+
+/* attn_status_str: static, NUL-terminated name of a status code ("ATTN_OK", ...). */
+const char* attn_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

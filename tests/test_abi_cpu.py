@@ -1,0 +1,156 @@
+"""The C ABI on the host: the library loads, exports what include/attn.h declares, and turns
+every argument error into its status code before anything touches a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import exact_softmax_attention_paged_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    return sorted(set(re.findall(r"^\S[^\n(]*?\b(attn_[a-z_]+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_python_names():
+    assert _declared() == sorted(A.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (attn_\w+)", out))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(A.lib(), name)
+
+
+def test_status_strings():
+    names = ["ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_BLOCK_SIZE", "ATTN_ERR_GQA",
+             "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE", "ATTN_ERR_METADATA", "ATTN_ERR_HIP"]
+    assert [A.attn_status_str(i) for i in range(9)] == names
+    assert A.attn_status_str(99) == "ATTN_ERR_UNKNOWN"
+
+
+def _desc(**kw):
+    base = dict(num_seqs=2, num_tokens=5, num_decodes=1, max_query_len=4, max_seq_len=40,
+                num_heads=8, num_kv_heads=2, head_size=128, num_blocks=8, block_size=16,
+                max_blocks_per_seq=3, dtype=A.ATTN_BF16, partition_tokens=0)
+    base.update(kw)
+    return A.make_desc(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+def _fwd(desc, causal=1, window=0, scale=0.125, ws=None, ws_bytes=0, q=FAKE, out=FAKE):
+    return A.lib().attn_varlen_fwd(ctypes.byref(desc), q, FAKE, FAKE, FAKE, FAKE, scale,
+                                   causal, window, out, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_size=24), A.ATTN_ERR_BLOCK_SIZE),
+    (dict(block_size=0), A.ATTN_ERR_BLOCK_SIZE),
+    (dict(num_heads=6, num_kv_heads=4), A.ATTN_ERR_GQA),
+    (dict(head_size=96), A.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=7), A.ATTN_ERR_UNSUPPORTED),
+    (dict(partition_tokens=100), A.ATTN_ERR_UNSUPPORTED),
+    (dict(num_decodes=3), A.ATTN_ERR_SHAPE),
+    (dict(num_tokens=-1), A.ATTN_ERR_SHAPE),
+    (dict(max_seq_len=49), A.ATTN_ERR_SHAPE),       # exceeds max_blocks_per_seq * block_size
+    (dict(max_query_len=41), A.ATTN_ERR_SHAPE),
+])
+def test_descriptor_errors(kw, status):
+    d = _desc(**kw)
+    assert _fwd(d) == status
+    n = ctypes.c_size_t(0)
+    assert A.lib().attn_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == status
+
+
+def test_window_needs_causal_and_scale_must_be_positive():
+    assert _fwd(_desc(), causal=0, window=8) == A.ATTN_ERR_UNSUPPORTED
+    assert _fwd(_desc(), scale=0.0) == A.ATTN_ERR_UNSUPPORTED
+    assert _fwd(_desc(), scale=float("nan")) == A.ATTN_ERR_UNSUPPORTED
+
+
+def test_null_pointers():
+    assert A.lib().attn_varlen_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 1, 0, FAKE, None,
+                                   None, 0, None) == A.ATTN_ERR_NULL
+    assert _fwd(_desc(), q=None) == A.ATTN_ERR_NULL
+    assert _fwd(_desc(), out=None) == A.ATTN_ERR_NULL
+    assert A.lib().attn_workspace_bytes(ctypes.byref(_desc()), None) == A.ATTN_ERR_NULL
+
+
+def test_workspace_size_and_check():
+    d = _desc(num_decodes=1, max_seq_len=40)
+    need = A.attn_workspace_bytes(d)
+    parts = -(-40 // 512)
+    assert need == -(-(1 * 8 * parts * 129 * 4) // 256) * 256
+    assert _fwd(d, ws=None, ws_bytes=0) == A.ATTN_ERR_WORKSPACE
+    assert _fwd(d, ws=FAKE, ws_bytes=need - 1) == A.ATTN_ERR_WORKSPACE
+    big = _desc(num_decodes=1, max_seq_len=40000, max_blocks_per_seq=2500)
+    parts = -(-40000 // 256)
+    assert A.attn_workspace_bytes(_desc(num_decodes=1, max_seq_len=40000, max_blocks_per_seq=2500,
+                                        partition_tokens=256)) == \
+        -(-(8 * parts * 129 * 4) // 256) * 256
+    assert A.attn_workspace_bytes(_desc(num_decodes=0)) == 0
+    assert A.attn_workspace_bytes(_desc(dtype=A.ATTN_F32)) == 0
+    assert big is not None
+
+
+def test_empty_batch_is_a_no_op():
+    d = _desc(num_seqs=0, num_tokens=0, num_decodes=0, max_query_len=0, max_seq_len=0)
+    assert _fwd(d, q=None, out=None) == A.ATTN_OK
+
+
+def _meta():
+    qsl = np.array([0, 1, 5], np.int32)
+    sl = np.array([17, 40], np.int32)
+    bt = np.array([[3, 4, 7], [0, 1, 2]], np.int32)
+    return bt, qsl, sl
+
+
+def test_metadata_checker_accepts_good_and_rejects_bad():
+    d = _desc()
+    bt, qsl, sl = _meta()
+    assert A.attn_check_metadata_host(d, bt, qsl, sl) == A.ATTN_OK
+    bad = []
+    b = bt.copy(); b[1, 2] = 8; bad.append((b, qsl, sl))              # block id out of range
+    b = bt.copy(); b[0, 1] = -1; bad.append((b, qsl, sl))
+    bad.append((bt, np.array([0, 2, 5], np.int32), sl))                 # decode row with ql 2
+    bad.append((bt, np.array([0, 1, 4], np.int32), sl))                 # ends before num_tokens
+    bad.append((bt, np.array([1, 1, 5], np.int32), sl))                 # does not start at 0
+    bad.append((bt, qsl, np.array([17, 3], np.int32)))                  # seq_len < query_len
+    bad.append((bt, qsl, np.array([17, 41], np.int32)))                 # > max_seq_len
+    for b, q, s in bad:
+        assert A.attn_check_metadata_host(d, b, q, s) == A.ATTN_ERR_METADATA
+    # an unused table entry may hold anything
+    b = bt.copy(); b[0, 2] = -5
+    assert A.attn_check_metadata_host(d, b, qsl, sl) == A.ATTN_OK
+
+
+def test_generated_workloads_pass_the_metadata_checker():
+    import gen
+    for k in (1, 2, 3, 4, 5):
+        b = gen.config(k)
+        d = A.make_desc(num_seqs=b.num_seqs, num_tokens=b.num_tokens, num_decodes=b.num_decodes,
+                        max_query_len=b.max_query_len, max_seq_len=b.max_seq_len,
+                        num_heads=b.num_heads, num_kv_heads=b.num_kv_heads,
+                        head_size=b.head_size, num_blocks=b.num_blocks,
+                        block_size=b.block_size, max_blocks_per_seq=b.max_blocks_per_seq,
+                        dtype=A.ATTN_BF16 if b.dtype == "bf16" else A.ATTN_F32)
+        assert A.attn_check_metadata_host(d, b.block_table, b.query_start_loc,
+                                          b.seq_lens) == A.ATTN_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(5, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        A.attn_varlen_fwd(_desc(), q, q, q, q, q, 0.1, True, 0, q, None, None)

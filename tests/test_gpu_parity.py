@@ -1,0 +1,113 @@
+"""Parity of the HIP path with the CPU oracle, element by element, on seeded inputs.
+
+Small batches (several tiles, ragged tails, every mask kind, GQA ratios 1..20, block sizes
+16..512, decode and prefill rows, NaN in every slot no request may read) are compared in
+full. The five workloads are run at full size in the bench's launch configuration and
+compared on all rows the oracle finishes in seconds (cfg1-3 in full, sampled requests and
+rows for cfg4 and cfg5)."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+from parity import compare, oracle_on, run_library
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _batch(seed, *, ql, sl, hq, hkv, d, bs, dtype="bf16", pool_factor=2, shared=0):
+    return gen.make_batch(f"case{seed}", num_heads=hq, num_kv_heads=hkv, head_size=d,
+                          block_size=bs, dtype=dtype, query_lens=ql, seq_lens=sl,
+                          passes=[(True, 0)], seed=seed, pool_factor=pool_factor,
+                          shared_prefix_blocks=shared)
+
+
+SMALL = [
+    # name, kwargs
+    ("prefill-d64-mha", dict(ql=[200, 1, 64, 129], sl=[200, 50, 300, 129], hq=4, hkv=4, d=64, bs=16)),
+    ("prefill-d128-gqa4", dict(ql=[77, 130, 5], sl=[300, 130, 900], hq=8, hkv=2, d=128, bs=32)),
+    ("decode-then-prefill-d128-gqa8", dict(ql=[1, 1, 1, 40, 300], sl=[1, 700, 1500, 1000, 300],
+                                           hq=16, hkv=2, d=128, bs=16)),
+    ("decode-d64-gqa20", dict(ql=[1, 1, 1], sl=[513, 2000, 64], hq=40, hkv=2, d=64, bs=64)),
+    ("decode-d128-g1-bs512", dict(ql=[1, 1, 9], sl=[1025, 511, 520], hq=3, hkv=3, d=128, bs=512)),
+]
+MASKS = [(False, 0), (True, 0), (True, 1), (True, 100), (True, 513)]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("causal,window", MASKS, ids=[f"c{int(c)}w{w}" for c, w in MASKS])
+def test_small_batches_match_oracle(name, kw, causal, window):
+    seed = zlib.crc32(name.encode()) % 1000
+    b = _batch(seed, **kw)
+    print(f"[case] {name} causal={causal} window={window} decodes={b.num_decodes}", flush=True)
+    q, kv = gen.make_tensors(b, seed, DEV, poison=True)
+    out, lse = run_library(b, q, kv, causal, window)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_on(b, q, kv, causal, window)
+    compare(out, lse, ref_out, ref_lse, label=name)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 37)])
+def test_f32_matches_oracle(d, causal, window):
+    b = _batch(5, ql=[100, 1, 33], sl=[100, 300, 200], hq=4, hkv=2, d=d, bs=16, dtype="f32")
+    q, kv = gen.make_tensors(b, 5, DEV, poison=True)
+    out, lse = run_library(b, q, kv, causal, window)
+    ref_out, ref_lse = oracle_on(b, q, kv, causal, window)
+    res = compare(out, lse, ref_out, ref_lse, label="f32")
+    assert res["out_max"] < 1e-4 and res["lse_max"] < 1e-4, res
+
+
+# ---------------------------------------------------------------- the five workloads
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_workload_full_parity(k):
+    b = gen.config(k)
+    causal, window = b.passes[0]
+    print(f"[case] cfg{k} full", flush=True)
+    q, kv = gen.make_tensors(b, k, DEV, poison=True)
+    out, lse = run_library(b, q, kv, causal, window)
+    ref_out, ref_lse = oracle_on(b, q, kv, causal, window)
+    print(compare(out, lse, ref_out, ref_lse, label=f"cfg{k}"))
+
+
+def _sampled_parity(b, q, kv, causal, window, requests, rows_per_request):
+    out, lse = run_library(b, q, kv, causal, window)
+    torch.cuda.synchronize()
+    sub, qs, kvs = gen.subset(b, requests, q, kv)
+    qsl_sub = sub.query_start_loc
+    rows_sub, rows_full = [], []
+    qsl = b.query_start_loc
+    for i, r in enumerate(requests):
+        ql = int(b.query_lens[r])
+        pick = np.unique(np.concatenate([[0, ql - 1], np.linspace(0, ql - 1, rows_per_request)
+                                         .astype(int)])) if ql > rows_per_request else np.arange(ql)
+        rows_sub.extend(qsl_sub[i] + pick)
+        rows_full.extend(qsl[r] + pick)
+    ref_out, ref_lse = oracle_on(sub, qs, kvs, causal, window, rows=rows_sub)
+    o = out[torch.as_tensor(rows_full, device=out.device)]
+    l = lse[torch.as_tensor(rows_full, device=out.device)]
+    return compare(o, l, ref_out[rows_sub], ref_lse[rows_sub], label=b.name)
+
+
+def test_workload4_sampled_parity():
+    b = gen.config(4)
+    print("[case] cfg4 full size, sampled requests", flush=True)
+    q, kv = gen.make_tensors(b, 4, DEV)
+    order = np.argsort(b.seq_lens)
+    req = sorted(set(order[:8].tolist() + order[-8:].tolist() +
+                     np.random.default_rng(0).choice(256, 32, replace=False).tolist()))
+    print(_sampled_parity(b, q, kv, True, 0, req, 1))
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_workload5_sampled_parity(layer):
+    b = gen.config(5)
+    causal, window = b.passes[layer]
+    print(f"[case] cfg5 layer {layer} full size, sampled", flush=True)
+    q, kv = gen.make_tensors(b, 5, DEV, layer=layer)
+    dec = np.argsort(b.seq_lens[:120])
+    req = sorted(set(dec[:4].tolist() + dec[-4:].tolist() + [17, 60, 99])) + list(range(120, 128))
+    print(_sampled_parity(b, q, kv, causal, window, req, 12))
