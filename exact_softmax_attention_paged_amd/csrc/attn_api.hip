@@ -30,11 +30,15 @@ attn_status check_desc(const attn_desc* d) {
   if (d->num_heads % d->num_kv_heads != 0) return ATTN_ERR_GQA;
   if (d->head_size != 64 && d->head_size != 128) return ATTN_ERR_UNSUPPORTED;
   if (d->dtype != ATTN_BF16 && d->dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
-  if (d->partition_tokens < 0 || (d->partition_tokens > 0 && d->partition_tokens % 128 != 0))
+  if (d->partition_tokens < 0 || d->partition_tokens > attn::kMaxPartitionTokens ||
+      (d->partition_tokens > 0 && d->partition_tokens % 128 != 0))
     return ATTN_ERR_UNSUPPORTED;
   if (d->num_seqs > 65535) return ATTN_ERR_SHAPE;                    // grid z limit
   if ((int64_t)d->max_seq_len > (int64_t)d->max_blocks_per_seq * d->block_size)
     return ATTN_ERR_SHAPE;
+  if ((int64_t)d->max_seq_len * d->block_size >= ((int64_t)1 << 40)) return ATTN_ERR_SHAPE;
+  if ((int64_t)d->block_size * d->num_kv_heads * d->head_size >= ((int64_t)1 << 31))
+    return ATTN_ERR_SHAPE;                                            // one block < 2^31 elements
   return ATTN_OK;
 }
 
@@ -111,6 +115,10 @@ attn_status attn_varlen_fwd(const attn_desc* desc, const void* q, const void* kv
   pp.causal = causal ? 1 : 0;
   pp.window = window > 0 ? window : 0;
   pp.scale = scale;
+  {
+    const uint64_t groups = (uint64_t)(d.block_size / 16);
+    pp.group_recip = (((uint64_t)1 << 32) + groups - 1) / groups;
+  }
 
   if (d.dtype == ATTN_F32) {
     // float32 runs every request, decode rows included, through the fp32 prefill kernel

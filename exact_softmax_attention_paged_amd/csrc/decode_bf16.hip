@@ -42,12 +42,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
   __shared__ float sM[kWaves][16];
   __shared__ float sL[kWaves][16];
+  __shared__ int32_t sBlk[kMaxPartitionTokens / 16];   // block ids of this partition
 
+  // grid: x = (kv head, head group) fastest, so that the workgroups reading the same tokens'
+  // rows (adjacent in every cache block) run side by side; y = partition; z = request
   const int r = blockIdx.z;
   const int group = p.num_heads / p.num_kv_heads;
   const int head_groups = (group + 15) / 16;
-  const int kvh = blockIdx.y / head_groups;
-  const int hg = blockIdx.y % head_groups;
+  const int kvh = blockIdx.x / head_groups;
+  const int hg = blockIdx.x % head_groups;
   const int nh = min(16, group - hg * 16);             // q heads in this workgroup
   const int h0 = kvh * group + hg * 16;                // first q head
 
@@ -55,12 +58,13 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   int first, nparts;
   decode_partitions(sl, p.window, p.part_tokens, &first, &nparts);
   nparts = min(nparts, p.max_parts);   // only reachable with seq_len > max_seq_len
-  const int pi = blockIdx.x;
+  const int pi = blockIdx.y;
   if (pi >= nparts) return;
   const int part = first + pi;
+  const int p_start = part * p.part_tokens;
   const int lo = p.window > 0 ? max(0, sl - p.window) : 0;
-  const int k_begin = max(lo, part * p.part_tokens);
-  const int k_end = min(sl, (part + 1) * p.part_tokens);
+  const int k_begin = max(lo, p_start);
+  const int k_end = min(sl, p_start + p.part_tokens);
   const int tok = p.qsl[r];
 
   const int tid = threadIdx.x;
@@ -69,10 +73,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   const int G = lane / 16;
   const int li = lane % 16;
 
+  // block ids covering [p_start, k_end) -> LDS, so the K/V loads need no dependent lookup
+  const int b_first = p_start / p.block_size;
+  const int n_blk = (k_end - 1) / p.block_size - b_first + 1;
+  const int32_t* __restrict__ bt = p.block_table + (int64_t)r * p.max_blocks;
+  for (int i = tid; i < n_blk; i += 256) sBlk[i] = bt[b_first + i];
+
   const __bf16* __restrict__ q = static_cast<const __bf16*>(p.q);
   const __bf16* __restrict__ kcache = static_cast<const __bf16*>(p.kv);
   const __bf16* __restrict__ vcache = kcache + p.v_offset;
-  const int32_t* __restrict__ bt = p.block_table + (int64_t)r * p.max_blocks;
 
   // Q^T (B operand): lane (G, li) holds q head h0 + li, d = 32c + 8G .. +7
   bf16x8 qf[KC];
@@ -85,11 +94,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
 
   // this wave's key range: quarter w of the partition, clipped to the visible range
   const int quarter = p.part_tokens / kWaves;
-  const int w_begin = max(k_begin, part * p.part_tokens + w * quarter);
-  const int w_end = min(k_end, part * p.part_tokens + (w + 1) * quarter);
-  // chunks are aligned to the quarter start (a multiple of 32), so a 16-key MFMA tile never
-  // straddles a block (block_size is a multiple of 16)
-  const int c_base = part * p.part_tokens + w * quarter;
+  const int w_begin = max(k_begin, p_start + w * quarter);
+  const int w_end = min(k_end, p_start + (w + 1) * quarter);
+  // chunks are aligned to the quarter start (a multiple of 32)
+  const int c_base = p_start + w * quarter;
   const int c_first = w_end > w_begin ? (w_begin - c_base) / kChunk : 0;
   const int n_chunks =
       w_end > w_begin ? (w_end - (c_base + c_first * kChunk) + kChunk - 1) / kChunk : 0;
@@ -97,33 +105,37 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   __bf16* sVw = reinterpret_cast<__bf16*>(lds) + w * V_TILE;
   const int v_row = lane / TPR;
   const int v_chunk = lane % TPR;
+  __syncthreads();   // sBlk ready
 
-  u32x4 kreg[2][KC], vreg[NV];
-  auto load_chunk = [&](int kb) {
+  struct Chunk {
+    u32x4 k[2][KC];
+    u32x4 v[NV];
+  };
+  auto row_off = [&](int key) {
+    const int32_t blk = sBlk[key / p.block_size - b_first];
+    return paged_row(blk, key % p.block_size, kvh, p.block_size, p.num_kv_heads, D);
+  };
+  auto load_chunk = [&](Chunk& ch, int kb) {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int key = kb + 16 * t2 + li;
-      if (key < sl) {
-        const int32_t blk = bt[key / p.block_size];
-        const int64_t off = paged_row(blk, key % p.block_size, kvh, p.block_size,
-                                      p.num_kv_heads, D) + 8 * G;
+      if (key < k_end) {
+        const int64_t off = row_off(key) + 8 * G;
 #pragma unroll
-        for (int c = 0; c < KC; ++c) kreg[t2][c] = *reinterpret_cast<const u32x4*>(kcache + off + 32 * c);
+        for (int c = 0; c < KC; ++c)
+          ch.k[t2][c] = *reinterpret_cast<const u32x4*>(kcache + off + 32 * c);
       } else {
 #pragma unroll
-        for (int c = 0; c < KC; ++c) kreg[t2][c] = u32x4{0, 0, 0, 0};
+        for (int c = 0; c < KC; ++c) ch.k[t2][c] = u32x4{0, 0, 0, 0};
       }
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int key = kb + j * RPI + v_row;
-      if (key < sl) {
-        const int32_t blk = bt[key / p.block_size];
-        const int64_t off = paged_row(blk, key % p.block_size, kvh, p.block_size,
-                                      p.num_kv_heads, D) + 8 * v_chunk;
-        vreg[j] = *reinterpret_cast<const u32x4*>(vcache + off);
+      if (key < k_end) {
+        ch.v[j] = *reinterpret_cast<const u32x4*>(vcache + row_off(key) + 8 * v_chunk);
       } else {
-        vreg[j] = u32x4{0, 0, 0, 0};   // past seq_len: zero so that 0 * V stays 0
+        ch.v[j] = u32x4{0, 0, 0, 0};   // past the partition / seq_len: 0 * V stays 0
       }
     }
   };
@@ -134,28 +146,22 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) o[dc] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  if (n_chunks > 0) load_chunk(c_base + c_first * kChunk);
-  for (int ci = 0; ci < n_chunks; ++ci) {
+  // consume chunk ci held in ch; after its QK^T MFMAs, refill ch with chunk ci + 2
+  auto consume = [&](Chunk& ch, int ci) {
     const int kb = c_base + (c_first + ci) * kChunk;
-    // V chunk -> wave-private LDS tile (row-major [key][d])
 #pragma unroll
     for (int j = 0; j < NV; ++j)
-      *reinterpret_cast<u32x4*>(&sVw[(j * RPI + v_row) * RS + 8 * v_chunk]) = vreg[j];
-    bf16x8 kf[2][KC];
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int c = 0; c < KC; ++c) kf[t2][c] = __builtin_bit_cast(bf16x8, kreg[t2][c]);
-    if (ci + 1 < n_chunks) load_chunk(kb + kChunk);
-
+      *reinterpret_cast<u32x4*>(&sVw[(j * RPI + v_row) * RS + 8 * v_chunk]) = ch.v[j];
     floatx4 sc[2];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < KC; ++c) acc = mfma16x16x32(kf[t2][c], qf[c], acc);
+      for (int c = 0; c < KC; ++c)
+        acc = mfma16x16x32(__builtin_bit_cast(bf16x8, ch.k[t2][c]), qf[c], acc);
       sc[t2] = acc;
     }
+    if (ci + 2 < n_chunks) load_chunk(ch, kb + 2 * kChunk);
     if (kb < w_begin || kb + kChunk > w_end) {
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
@@ -165,7 +171,6 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
           if (j < w_begin || j >= w_end) sc[t2][e] = -INFINITY;
         }
     }
-
     float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
     mx = column_max(mx);
@@ -198,6 +203,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
     }
     // the next chunk's LDS writes must not pass these reads
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+
+  // two chunks in flight per wave
+  Chunk bufA, bufB;
+  if (n_chunks > 0) load_chunk(bufA, c_base + c_first * kChunk);
+  if (n_chunks > 1) load_chunk(bufB, c_base + (c_first + 1) * kChunk);
+  for (int ci = 0; ci < n_chunks; ci += 2) {
+    consume(bufA, ci);
+    if (ci + 1 < n_chunks) consume(bufB, ci + 1);
   }
 
   // ---- combine the 4 waves: (m, l, O^T) -> partition result
@@ -297,7 +311,7 @@ template <int D>
 hipError_t launch(const DecodeParams& p, hipStream_t stream) {
   const int group = p.num_heads / p.num_kv_heads;
   const int head_groups = (group + 15) / 16;
-  const dim3 grid(p.max_parts, p.num_kv_heads * head_groups, p.num_decodes);
+  const dim3 grid(p.num_kv_heads * head_groups, p.max_parts, p.num_decodes);
   hipLaunchKernelGGL(decode_split_kernel<D>, grid, dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.max_parts <= 1) return e;

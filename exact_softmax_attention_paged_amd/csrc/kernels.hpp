@@ -5,6 +5,10 @@
 
 namespace attn {
 
+// Largest split-KV partition the decode kernel accepts (its block-id table holds
+// kMaxPartitionTokens / 16 entries).
+constexpr int32_t kMaxPartitionTokens = 4096;
+
 // One prefill launch covers requests [seq_begin, seq_begin + num_seqs) and every q head.
 struct PrefillParams {
   const void* q;                // [num_tokens][num_heads][head_size]
@@ -19,6 +23,8 @@ struct PrefillParams {
   int32_t seq_begin, num_seqs, max_query_len;
   int32_t causal, window;
   float scale;
+  uint64_t group_recip;         // ceil(2^32 / (block_size / 16)): block index of key k is
+                                // ((k / 16) * group_recip) >> 32 for k * block_size < 2^40
 };
 
 // One split-KV decode launch covers requests [0, num_decodes): each has query_len == 1.

@@ -7,47 +7,54 @@
 // FlashAttentionBackend section; GQA follows num_queries_per_kv of the FlashAttentionImpl
 // section; causal and sliding-window masks follow the RBLN "Attention 모드" page.
 //
-// Work split: one workgroup = 4 waves = 128 query rows of one (request, q head); each wave owns
-// 32 rows (two 16-row MFMA columns). KV is walked in 64-key tiles. Per tile:
-//   * all 256 threads gather the K and V rows (16-byte loads, one block-table lookup per row)
-//     into row-major LDS tiles; the next tile's loads are issued before this tile's math;
+// Work split: one workgroup = 4 waves of one (request, q head); each wave owns ROWS = 16*QS
+// query rows (QS 16-row MFMA columns), so a workgroup covers 4*ROWS rows. KV is walked in
+// 64-key tiles through two LDS buffers:
+//   * all 256 threads gather the next tile's K and V rows (16-byte loads, block index from a
+//     host-computed reciprocal) into registers while the current tile is consumed, then store
+//     them into the other buffer; one barrier per tile;
 //   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (K from LDS as the A operand, Q^T held in
 //     registers as the B operand), so each lane holds 4 keys of one query: the row max and row
 //     sum need only the 4 lanes of a column (v_permlane16/32_swap);
 //   * P^T stays in registers and is already in the B-operand layout of the next MFMA;
 //   * O^T += V^T . P^T, with V^T read straight from the row-major V tile by
 //     ds_read_b64_tr_b16, so no transpose pass is needed;
-//   * each lane owns one query column of O^T, so the online-softmax rescale is lane-local.
+//   * each lane owns one query column of O^T, so the softmax rescale is lane-local. The
+//     reference max is only moved when a new score exceeds it by more than 2^8 (in exp2
+//     units): the result O / l is the same for any reference, the skipped rescales save most
+//     of the per-tile VALU work, and p = 2^(s*c - m*c) stays <= 256.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace attn {
 namespace {
 
-constexpr int kBR = 128;      // query rows per workgroup
 constexpr int kBC = 64;       // keys per KV tile
 constexpr int kWaves = 4;
-constexpr int kRowsPerWave = kBR / kWaves;   // 32
-constexpr int kQS = kRowsPerWave / 16;       // 16-row MFMA columns per wave
+constexpr float kRescaleLog2 = 8.f;
 
-template <int D, bool CAUSAL, bool WINDOW>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillParams p) {
+
+template <int D, int QS, bool CAUSAL, bool WINDOW>
+__global__ __launch_bounds__(256, QS == 4 ? 1 : 2) void prefill_bf16_kernel(const PrefillParams p) {
+  constexpr int ROWS = 16 * QS;       // query rows per wave
+  constexpr int BR = kWaves * ROWS;   // query rows per workgroup
   constexpr int RS = D + 16;          // LDS row stride in bf16 (padding against bank conflicts)
   constexpr int KC = D / 32;          // k-chunks of the QK^T contraction
   constexpr int DC = D / 16;          // 16-wide d chunks of O^T
   constexpr int TPR = D / 8;          // threads per K/V row in the gather (16 bytes each)
   constexpr int RPP = 256 / TPR;      // rows per gather pass
   constexpr int NP = kBC / RPP;       // gather passes per tile
+  constexpr int TILE = kBC * RS;
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[kBC * RS];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[kBC * RS];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2 * TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2 * TILE];
 
   const int r = p.seq_begin + blockIdx.z;
   const int h = blockIdx.y;
   const int qt = gridDim.x - 1 - blockIdx.x;   // longest (causal) tiles are dispatched first
   const int q_start = p.qsl[r];
   const int ql = p.qsl[r + 1] - q_start;
-  if (qt * kBR >= ql) return;
+  if (qt * BR >= ql) return;
   const int sl = p.seq_lens[r];
   const int cl = sl - ql;
   const int kvh = h / (p.num_heads / p.num_kv_heads);
@@ -65,167 +72,196 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillParam
   const int64_t row_stride = (int64_t)p.num_heads * D;   // q/out stride between tokens
 
   // ---- Q^T fragments (B operand): lane (G, li) holds query li, d = 32c + 8G .. +7
-  bf16x8 qf[kQS][KC];
-  const int wrow0 = qt * kBR + w * kRowsPerWave;        // first query row of this wave
+  bf16x8 qf[QS][KC];
+  const int wrow0 = qt * BR + w * ROWS;                 // first query row of this wave
 #pragma unroll
-  for (int s = 0; s < kQS; ++s) {
-    const int row = wrow0 + s * 16 + li;
+  for (int s = 0; s < QS; ++s) {
+    const int row = min(wrow0 + s * 16 + li, ql - 1);   // rows past ql: any valid row
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      if (row < ql) {
-        qf[s][c] = *reinterpret_cast<const bf16x8*>(q + (int64_t)(q_start + row) * row_stride +
-                                                    (int64_t)h * D + 32 * c + 8 * G);
-      } else {
-        qf[s][c] = bf16x8{};
-      }
-    }
+    for (int c = 0; c < KC; ++c)
+      qf[s][c] = *reinterpret_cast<const bf16x8*>(q + (int64_t)(q_start + row) * row_stride +
+                                                  (int64_t)h * D + 32 * c + 8 * G);
   }
 
   // ---- KV range of the workgroup and of this wave
-  const int row_lo = qt * kBR;
-  const int row_hi = min(ql, row_lo + kBR) - 1;
+  const int row_lo = qt * BR;
+  const int row_hi = min(ql, row_lo + BR) - 1;
   const int kv_hi = CAUSAL ? min(sl, cl + row_hi + 1) : sl;
   const int kv_lo = WINDOW ? max(0, cl + row_lo - p.window + 1) : 0;
   const int t_begin = kv_lo / kBC;
   const int t_end = (kv_hi + kBC - 1) / kBC;
   const int w_row_lo = wrow0;
-  const int w_row_hi = min(ql, wrow0 + kRowsPerWave) - 1;
+  const int w_row_hi = min(ql, wrow0 + ROWS) - 1;
   const bool wave_active = w_row_lo <= w_row_hi;
   const int w_kv_hi = CAUSAL ? min(sl, cl + w_row_hi + 1) : sl;
   const int w_kv_lo = WINDOW ? max(0, cl + w_row_lo - p.window + 1) : 0;
 
-  // ---- gather assignment: thread -> (row in pass, 16-byte chunk)
+  // ---- gather: thread -> (row in pass, 16-byte chunk). The block index of key k is
+  // (k / 16) / (block_size / 16), computed with the host's 32.32 reciprocal; block ids are
+  // fetched one tile ahead of the K/V rows so that no load waits on another.
   const int g_row = tid / TPR;
   const int g_chunk = tid % TPR;
-  u32x4 kreg[NP], vreg[NP];
-  auto gather = [&](int tile) {
+  const uint32_t block_elems = (uint32_t)(p.block_size * p.num_kv_heads * D);   // < 2^31
+  const int kv_row = p.num_kv_heads * D;
+  const int head_off = kvh * D + g_chunk * 8;
+  int32_t blk_next[NP];     // block ids of the tile to gather next
+  int32_t slot_next[NP];
+  auto fetch_blocks = [&](int tile) {
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) {
-      const int key = tile * kBC + pp * RPP + g_row;
-      if (key < sl) {
-        const int32_t blk = bt[key / p.block_size];
-        const int64_t off = paged_row(blk, key % p.block_size, kvh, p.block_size,
-                                      p.num_kv_heads, D) + g_chunk * 8;
-        kreg[pp] = *reinterpret_cast<const u32x4*>(kcache + off);
-        vreg[pp] = *reinterpret_cast<const u32x4*>(vcache + off);
-      } else {
-        kreg[pp] = u32x4{0, 0, 0, 0};   // keys past seq_len: zero, never NaN from stale slots
-        vreg[pp] = u32x4{0, 0, 0, 0};
+      const int kk = min(tile * kBC + pp * RPP + g_row, sl - 1);   // a valid row of the request
+      const uint32_t bidx = (uint32_t)(((uint64_t)(uint32_t)(kk >> 4) * p.group_recip) >> 32);
+      blk_next[pp] = bt[bidx];
+      slot_next[pp] = kk - (int)bidx * p.block_size;
+    }
+  };
+  u32x4 kreg[NP], vreg[NP];
+  auto gather = [&]() {       // K/V rows of the tile whose block ids are in blk_next
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+      const uint64_t off = (uint64_t)(uint32_t)blk_next[pp] * block_elems +
+                           (uint32_t)(slot_next[pp] * kv_row + head_off);
+      kreg[pp] = *reinterpret_cast<const u32x4*>(kcache + off);
+      vreg[pp] = *reinterpret_cast<const u32x4*>(vcache + off);
+    }
+  };
+  auto stash = [&](int buf, int tile) {
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+      u32x4 kx = kreg[pp], vx = vreg[pp];
+      if (tile * kBC + pp * RPP + g_row >= sl) {   // keys past seq_len: zero, never stale slots
+        kx = u32x4{0, 0, 0, 0};
+        vx = u32x4{0, 0, 0, 0};
       }
+      *reinterpret_cast<u32x4*>(&sK[buf * TILE + (pp * RPP + g_row) * RS + g_chunk * 8]) = kx;
+      *reinterpret_cast<u32x4*>(&sV[buf * TILE + (pp * RPP + g_row) * RS + g_chunk * 8]) = vx;
     }
   };
 
   const float c_log2 = p.scale * kLog2e;
-  float m_run[kQS], l_run[kQS];
-  floatx4 o[kQS][DC];
+  float m_ref[QS], l_run[QS];
+  floatx4 o[QS][DC];
 #pragma unroll
-  for (int s = 0; s < kQS; ++s) {
-    m_run[s] = -INFINITY;
+  for (int s = 0; s < QS; ++s) {
+    m_ref[s] = -INFINITY;
     l_run[s] = 0.f;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) o[s][dc] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  if (t_begin < t_end) gather(t_begin);
+  if (t_begin < t_end) {
+    fetch_blocks(t_begin);
+    gather();
+    if (t_begin + 1 < t_end) fetch_blocks(t_begin + 1);
+    stash(0, t_begin);
+  }
+  __syncthreads();
   for (int t = t_begin; t < t_end; ++t) {
-    __syncthreads();   // every wave is done reading the previous tile
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp) {
-      *reinterpret_cast<u32x4*>(&sK[(pp * RPP + g_row) * RS + g_chunk * 8]) = kreg[pp];
-      *reinterpret_cast<u32x4*>(&sV[(pp * RPP + g_row) * RS + g_chunk * 8]) = vreg[pp];
+    const int buf = (t - t_begin) & 1;
+    const bool more = t + 1 < t_end;
+    if (more) {                  // in flight while this tile is consumed
+      gather();
+      if (t + 2 < t_end) fetch_blocks(t + 2);
     }
-    __syncthreads();
-    if (t + 1 < t_end) gather(t + 1);
 
     const int kb = t * kBC;
-    if (!wave_active || kb >= w_kv_hi || kb + kBC <= w_kv_lo) continue;
-
-    // S^T tiles: s[s][kt] holds keys kb + 16kt + 4G + e of query column li
-    floatx4 sc[kQS][4];
+    if (wave_active && kb < w_kv_hi && kb + kBC > w_kv_lo) {
+      const __bf16* tK = sK + buf * TILE;
+      const __bf16* tV = sV + buf * TILE;
+      // S^T tiles: sc[s][kt] holds keys kb + 16kt + 4G + e of query column li
+      floatx4 sc[QS][4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      bf16x8 kf[KC];
+      for (int kt = 0; kt < 4; ++kt) {
+        bf16x8 kf[KC];
 #pragma unroll
-      for (int c = 0; c < KC; ++c)
-        kf[c] = *reinterpret_cast<const bf16x8*>(&sK[(kt * 16 + li) * RS + 32 * c + 8 * G]);
+        for (int c = 0; c < KC; ++c)
+          kf[c] = *reinterpret_cast<const bf16x8*>(&tK[(kt * 16 + li) * RS + 32 * c + 8 * G]);
 #pragma unroll
-      for (int s = 0; s < kQS; ++s) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < QS; ++s) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < KC; ++c) acc = mfma16x16x32(kf[c], qf[s][c], acc);
-        sc[s][kt] = acc;
+          for (int c = 0; c < KC; ++c) acc = mfma16x16x32(kf[c], qf[s][c], acc);
+          sc[s][kt] = acc;
+        }
       }
-    }
 
-    const bool need_mask = (kb + kBC > sl) || (CAUSAL && kb + kBC - 1 > cl + w_row_lo) ||
-                           (WINDOW && kb < cl + w_row_hi - p.window + 1);
-    if (need_mask) {
+      const bool need_mask = (kb + kBC > sl) || (CAUSAL && kb + kBC - 1 > cl + w_row_lo) ||
+                             (WINDOW && kb < cl + w_row_hi - p.window + 1);
+      if (need_mask) {
 #pragma unroll
-      for (int s = 0; s < kQS; ++s) {
-        const int pos = cl + wrow0 + s * 16 + li;   // absolute position of this query
+        for (int s = 0; s < QS; ++s) {
+          const int pos = cl + wrow0 + s * 16 + li;   // absolute position of this query
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int j = kb + kt * 16 + 4 * G + e;
+              bool vis = j < sl;
+              if (CAUSAL) vis = vis && (j <= pos);
+              if (WINDOW) vis = vis && (j >= pos - p.window + 1);
+              if (!vis) sc[s][kt][e] = -INFINITY;
+            }
+        }
+      }
+
+      // online softmax with a lazily moved reference max, one query column per lane
+#pragma unroll
+      for (int s = 0; s < QS; ++s) {
+        float mx = fmaxf(fmaxf(sc[s][0][0], sc[s][0][1]), fmaxf(sc[s][0][2], sc[s][0][3]));
+#pragma unroll
+        for (int kt = 1; kt < 4; ++kt)
+          mx = fmaxf(mx, fmaxf(fmaxf(sc[s][kt][0], sc[s][kt][1]),
+                               fmaxf(sc[s][kt][2], sc[s][kt][3])));
+        mx = column_max(mx);
+        // move the reference when the tile max exceeds it by more than 2^kRescaleLog2
+        // (always on the first visible tile, where m_ref is -inf)
+        const bool move = (mx - m_ref[s]) * c_log2 > kRescaleLog2;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+          // alpha is 0 when m_ref was -inf; columns that keep their reference use 1
+          const float alpha = move ? fast_exp2((m_ref[s] - mx) * c_log2) : 1.f;
+          if (move) m_ref[s] = mx;
+          l_run[s] *= alpha;
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc) o[s][dc] *= alpha;
+        }
+        const float mc = (m_ref[s] == -INFINITY) ? 0.f : m_ref[s] * c_log2;
+        float lsum = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int j = kb + kt * 16 + 4 * G + e;
-            bool vis = j < sl;
-            if (CAUSAL) vis = vis && (j <= pos);
-            if (WINDOW) vis = vis && (j >= pos - p.window + 1);
-            if (!vis) sc[s][kt][e] = -INFINITY;
+            const float pv = fast_exp2(fmaf(sc[s][kt][e], c_log2, -mc));
+            sc[s][kt][e] = pv;
+            lsum += pv;
           }
+        l_run[s] += lsum;
       }
-    }
 
-    // online softmax, one query column per lane
+      // O^T += V^T . P^T over two 32-key halves
 #pragma unroll
-    for (int s = 0; s < kQS; ++s) {
-      float mx = sc[s][0][0];
+      for (int hk = 0; hk < 2; ++hk) {
+        bf16x8 pb[QS];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+        for (int s = 0; s < QS; ++s) pb[s] = pack_bf16x8(sc[s][2 * hk], sc[s][2 * hk + 1]);
+        const int r0 = 32 * hk + 4 * G + li / 4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[s][kt][e]);
-      mx = column_max(mx);
-      const float m_new = fmaxf(m_run[s], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run[s] - m_use) * c_log2);
-      const float mc = m_use * c_log2;
-      float lsum = 0.f;
+        for (int dc = 0; dc < DC; ++dc) {
+          const int col = 16 * dc + 4 * (li % 4);
+          const bf16x8 va = concat(lds_read_tr16(&tV[r0 * RS + col]),
+                                   lds_read_tr16(&tV[(r0 + 16) * RS + col]));
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pv = fast_exp2(fmaf(sc[s][kt][e], c_log2, -mc));
-          sc[s][kt][e] = pv;
-          lsum += pv;
+          for (int s = 0; s < QS; ++s) o[s][dc] = mfma16x16x32(va, pb[s], o[s][dc]);
         }
-      l_run[s] = l_run[s] * alpha + lsum;
-      m_run[s] = m_new;
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) o[s][dc] *= alpha;
-    }
-
-    // O^T += V^T . P^T over two 32-key halves
-#pragma unroll
-    for (int hk = 0; hk < 2; ++hk) {
-      bf16x8 pb[kQS];
-#pragma unroll
-      for (int s = 0; s < kQS; ++s) pb[s] = pack_bf16x8(sc[s][2 * hk], sc[s][2 * hk + 1]);
-      const int r0 = 32 * hk + 4 * G + li / 4;
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const int col = 16 * dc + 4 * (li % 4);
-        const bf16x8 va = concat(lds_read_tr16(&sV[r0 * RS + col]),
-                                 lds_read_tr16(&sV[(r0 + 16) * RS + col]));
-#pragma unroll
-        for (int s = 0; s < kQS; ++s) o[s][dc] = mfma16x16x32(va, pb[s], o[s][dc]);
       }
     }
+    if (more) stash(buf ^ 1, t + 1);
+    __syncthreads();
   }
 
   // ---- epilogue: O / l and lse = scale * m + ln l
   __bf16* __restrict__ out = static_cast<__bf16*>(p.out);
 #pragma unroll
-  for (int s = 0; s < kQS; ++s) {
+  for (int s = 0; s < QS; ++s) {
     const float l_tot = column_sum(l_run[s]);
     const int row = wrow0 + s * 16 + li;
     if (row >= ql) continue;
@@ -242,30 +278,39 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillParam
     }
     if (p.lse != nullptr && G == 0) {
       p.lse[(int64_t)(q_start + row) * p.num_heads + h] =
-          l_tot > 0.f ? p.scale * m_run[s] + __logf(l_tot) : -INFINITY;
+          l_tot > 0.f ? p.scale * m_ref[s] + __logf(l_tot) : -INFINITY;
     }
   }
 }
 
-template <int D, bool CAUSAL, bool WINDOW>
+template <int D, int QS, bool CAUSAL, bool WINDOW>
 hipError_t launch(const PrefillParams& p, hipStream_t stream) {
-  const dim3 grid((p.max_query_len + kBR - 1) / kBR, p.num_heads, p.num_seqs);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, WINDOW>), grid, dim3(256), 0, stream, p);
+  constexpr int BR = kWaves * 16 * QS;
+  const dim3 grid((p.max_query_len + BR - 1) / BR, p.num_heads, p.num_seqs);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, QS, CAUSAL, WINDOW>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int QS>
 hipError_t launch_mask(const PrefillParams& p, hipStream_t stream) {
-  if (p.window > 0) return launch<D, true, true>(p, stream);
-  if (p.causal) return launch<D, true, false>(p, stream);
-  return launch<D, false, false>(p, stream);
+  if (p.window > 0) return launch<D, QS, true, true>(p, stream);
+  if (p.causal) return launch<D, QS, true, false>(p, stream);
+  return launch<D, QS, false, false>(p, stream);
+}
+
+template <int D>
+hipError_t launch_rows(const PrefillParams& p, hipStream_t stream) {
+  // 32 rows per wave. 64 rows per wave (QS = 4, one wave per SIMD) halves the LDS bytes per
+  // MFMA but measured 27 % (d 128) to 48 % (d 64) slower on the workloads here: with a single
+  // wave per SIMD nothing hides the softmax and LDS latency between the two MFMA phases.
+  return launch_mask<D, 2>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   if (p.num_seqs <= 0 || p.max_query_len <= 0) return hipSuccess;
-  return p.head_size == 64 ? launch_mask<64>(p, stream) : launch_mask<128>(p, stream);
+  return p.head_size == 64 ? launch_rows<64>(p, stream) : launch_rows<128>(p, stream);
 }
 
 }  // namespace attn

@@ -81,7 +81,7 @@ typedef struct attn_desc {
   int32_t max_blocks_per_seq; /* row stride of block_table */
   int32_t dtype;              /* attn_dtype */
   int32_t partition_tokens;   /* split-KV partition length for decode rows: 0 means 512;
-                                 otherwise a positive multiple of 128 */
+                                 otherwise a multiple of 128 in [128, 4096] */
 } attn_desc;
 
 /*
@@ -132,7 +132,8 @@ attn_status attn_workspace_bytes(const attn_desc* desc, size_t* bytes);
  *
  * Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_BLOCK_SIZE ([FA] Backend raises on
  * block_size % 16 != 0), ATTN_ERR_GQA, ATTN_ERR_UNSUPPORTED (head_size not 64/128, unknown
- * dtype, partition_tokens not a multiple of 128, window > 0 without causal),
+ * dtype, partition_tokens not a multiple of 128 in [128, 4096], window > 0 without
+ * causal, scale not finite and > 0),
  * ATTN_ERR_WORKSPACE, ATTN_ERR_HIP (launch failure).
  */
 attn_status attn_varlen_fwd(const attn_desc* desc, const void* q, const void* kv_cache,

@@ -51,6 +51,19 @@ def test_small_batches_match_oracle(name, kw, causal, window):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 300)])
+def test_large_prefill_matches_oracle(d, causal, window):
+    """Enough query tiles that the prefill kernel takes its 64-rows-per-wave variant."""
+    b = _batch(11, ql=[1024, 1000, 777, 1024], sl=[1024, 1300, 2000, 1100], hq=32, hkv=8, d=d,
+               bs=32)
+    print(f"[case] large prefill d={d} causal={causal} window={window}", flush=True)
+    q, kv = gen.make_tensors(b, 11, DEV, poison=True)
+    out, lse = run_library(b, q, kv, causal, window)
+    ref_out, ref_lse = oracle_on(b, q, kv, causal, window)
+    compare(out, lse, ref_out, ref_lse, label="large prefill")
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 37)])
 def test_f32_matches_oracle(d, causal, window):
     b = _batch(5, ql=[100, 1, 33], sl=[100, 300, 200], hq=4, hkv=2, d=d, bs=16, dtype="f32")
