@@ -96,51 +96,66 @@ __global__ __launch_bounds__(256, QS == 4 ? 1 : 2) void prefill_bf16_kernel(cons
   const int w_kv_hi = CAUSAL ? min(sl, cl + w_row_hi + 1) : sl;
   const int w_kv_lo = WINDOW ? max(0, cl + w_row_lo - p.window + 1) : 0;
 
-  // ---- gather: thread -> (row in pass, 16-byte chunk). The block index of key k is
-  // (k / 16) / (block_size / 16), computed with the host's 32.32 reciprocal; block ids are
-  // fetched one tile ahead of the K/V rows so that no load waits on another.
+  // ---- gather: thread -> (row in pass, 16-byte chunk). The rows one wave gathers in a pass
+  // lie in one 16-key group, and a 16-key group lies in one cache block (block_size is a
+  // multiple of 16), so the block lookup is wave-uniform: scalar loads of the block table,
+  // one tile ahead of the K/V rows. Block index of group g: g / (block_size / 16), computed
+  // with the host's 32.32 reciprocal.
+  constexpr int RPW = kWave / TPR;    // rows per wave per pass (4 or 8: divides 16)
   const int g_row = tid / TPR;
   const int g_chunk = tid % TPR;
   const uint32_t block_elems = (uint32_t)(p.block_size * p.num_kv_heads * D);   // < 2^31
   const int kv_row = p.num_kv_heads * D;
-  const int head_off = kvh * D + g_chunk * 8;
-  int32_t blk_next[NP];     // block ids of the tile to gather next
-  int32_t slot_next[NP];
+  const int groups_per_block = p.block_size / 16;
+  const int last_group = (sl - 1) >> 4;
+  uint64_t blk_off[NP];     // element offset of the 16-key group each pass reads (uniform)
   auto fetch_blocks = [&](int tile) {
+    int grp[NP];
+    uint32_t bidx[NP];
+    int32_t blk[NP];
 #pragma unroll
-    for (int pp = 0; pp < NP; ++pp) {
-      const int kk = min(tile * kBC + pp * RPP + g_row, sl - 1);   // a valid row of the request
-      const uint32_t bidx = (uint32_t)(((uint64_t)(uint32_t)(kk >> 4) * p.group_recip) >> 32);
-      blk_next[pp] = bt[bidx];
-      slot_next[pp] = kk - (int)bidx * p.block_size;
+    for (int pp = 0; pp < NP; ++pp) {   // all table loads first, then one wait
+      grp[pp] = min(__builtin_amdgcn_readfirstlane((tile * kBC + pp * RPP + w * RPW) >> 4),
+                    last_group);                     // groups past seq_len: any valid group
+      bidx[pp] = (uint32_t)(((uint64_t)(uint32_t)grp[pp] * p.group_recip) >> 32);
+      blk[pp] = bt[bidx[pp]];
     }
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp)
+      blk_off[pp] = (uint64_t)(uint32_t)blk[pp] * block_elems +
+                    (uint32_t)((grp[pp] - (int)bidx[pp] * groups_per_block) * 16 * kv_row);
   };
   u32x4 kreg[NP], vreg[NP];
-  auto gather = [&]() {       // K/V rows of the tile whose block ids are in blk_next
+  auto gather = [&]() {       // K/V rows of the tile whose groups are in blk_off
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) {
-      const uint64_t off = (uint64_t)(uint32_t)blk_next[pp] * block_elems +
-                           (uint32_t)(slot_next[pp] * kv_row + head_off);
-      kreg[pp] = *reinterpret_cast<const u32x4*>(kcache + off);
-      vreg[pp] = *reinterpret_cast<const u32x4*>(vcache + off);
+      const uint32_t lane_off =
+          (uint32_t)((((pp * RPP + w * RPW) & 15) + lane / TPR) * kv_row + kvh * D + g_chunk * 8);
+      kreg[pp] = *reinterpret_cast<const u32x4*>(kcache + blk_off[pp] + lane_off);
+      vreg[pp] = *reinterpret_cast<const u32x4*>(vcache + blk_off[pp] + lane_off);
     }
   };
   auto stash = [&](int buf, int tile) {
+    if (tile * kBC + kBC > sl) {                     // tail tile: zero keys past seq_len
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        if (tile * kBC + pp * RPP + g_row >= sl) {
+          kreg[pp] = u32x4{0, 0, 0, 0};
+          vreg[pp] = u32x4{0, 0, 0, 0};
+        }
+      }
+    }
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) {
-      u32x4 kx = kreg[pp], vx = vreg[pp];
-      if (tile * kBC + pp * RPP + g_row >= sl) {   // keys past seq_len: zero, never stale slots
-        kx = u32x4{0, 0, 0, 0};
-        vx = u32x4{0, 0, 0, 0};
-      }
-      *reinterpret_cast<u32x4*>(&sK[buf * TILE + (pp * RPP + g_row) * RS + g_chunk * 8]) = kx;
-      *reinterpret_cast<u32x4*>(&sV[buf * TILE + (pp * RPP + g_row) * RS + g_chunk * 8]) = vx;
+      *reinterpret_cast<u32x4*>(&sK[buf * TILE + (pp * RPP + g_row) * RS + g_chunk * 8]) = kreg[pp];
+      *reinterpret_cast<u32x4*>(&sV[buf * TILE + (pp * RPP + g_row) * RS + g_chunk * 8]) = vreg[pp];
     }
   };
 
   const float c_log2 = p.scale * kLog2e;
-  float m_ref[QS], l_run[QS];
+  float m_ref[QS];
   floatx4 o[QS][DC];
+  float l_run[QS];     // per-lane partial row sums (fp32: the lse needs them unrounded)
 #pragma unroll
   for (int s = 0; s < QS; ++s) {
     m_ref[s] = -INFINITY;
@@ -207,11 +222,10 @@ __global__ __launch_bounds__(256, QS == 4 ? 1 : 2) void prefill_bf16_kernel(cons
       // online softmax with a lazily moved reference max, one query column per lane
 #pragma unroll
       for (int s = 0; s < QS; ++s) {
-        float mx = fmaxf(fmaxf(sc[s][0][0], sc[s][0][1]), fmaxf(sc[s][0][2], sc[s][0][3]));
+        float mx = __builtin_fmaxf(sc[s][0][0], sc[s][0][1]);
 #pragma unroll
-        for (int kt = 1; kt < 4; ++kt)
-          mx = fmaxf(mx, fmaxf(fmaxf(sc[s][kt][0], sc[s][kt][1]),
-                               fmaxf(sc[s][kt][2], sc[s][kt][3])));
+        for (int x = 2; x < 16; x += 2)
+          mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[s][x / 4][x % 4]), sc[s][x / 4][x % 4 + 1]);
         mx = column_max(mx);
         // move the reference when the tile max exceeds it by more than 2^kRescaleLog2
         // (always on the first visible tile, where m_ref is -inf)
@@ -230,9 +244,8 @@ __global__ __launch_bounds__(256, QS == 4 ? 1 : 2) void prefill_bf16_kernel(cons
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float pv = fast_exp2(fmaf(sc[s][kt][e], c_log2, -mc));
-            sc[s][kt][e] = pv;
-            lsum += pv;
+            sc[s][kt][e] = fast_exp2(fmaf(sc[s][kt][e], c_log2, -mc));
+            lsum += sc[s][kt][e];
           }
         l_run[s] += lsum;
       }
