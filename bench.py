@@ -118,6 +118,82 @@ def cpu_baseline(batch, layers, seed):
                       f"time of that work / CPU time"}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
+PREFILL_SRC = os.path.join(ROOT, "exact_softmax_attention_paged_amd", "csrc", "prefill_bf16.hip")
+COPY_BYTES = 1 << 30
+
+
+def prefill_source_hash() -> str:
+    import hashlib
+    return hashlib.sha256(open(PREFILL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def pmc_probe(dev):
+    """Workload for the traffic counters: three plain 1 GiB device copies (the calibration
+    kernel of known size), then one bench step. Run under rocprofv3 --pmc FETCH_SIZE, then
+    --pmc WRITE_SIZE."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def record_traffic(fetch_csv, write_csv, command):
+    """Turn two rocprofv3 counter_collection.csv files into profiles/prefill_traffic.json:
+    per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of the prefill kernel, scaled by the bytes
+    the same counters report for the plain 1 GiB copy."""
+    import csv
+    import re
+
+    def per_kernel(path, counter):
+        acc = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            acc.setdefault(name, []).append(float(row["Counter_Value"]))
+        return acc
+
+    out = {"source_sha256_16": prefill_source_hash(), "command": command}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        acc = per_kernel(path, counter)
+        # the calibration copies are the runtime's device-to-device copy kernel
+        copy = sorted(v for n, vals in acc.items() if "rocclr_copyBuffer" in n for v in vals)
+        pre = {re.sub(r"\(attn::.*$", "", n.replace("void ", "").replace(
+            "attn::(anonymous namespace)::", "")): vals for n, vals in acc.items()
+            if "prefill_bf16_kernel" in n}
+        copy_kib = copy[len(copy) // 2]
+        expected_kib = COPY_BYTES / 1024.0
+        factor = expected_kib / copy_kib
+        out[counter] = {"copy_kib_per_dispatch": copy_kib, "copy_expected_kib": expected_kib,
+                        "scale": factor,
+                        "prefill_kib_per_dispatch": {k: sum(v) / len(v) for k, v in pre.items()}}
+    # per launch of the dominant kernel (the causal prefill of layer pass 0)
+    f_kib = out["FETCH_SIZE"]["prefill_kib_per_dispatch"]
+    w_kib = out["WRITE_SIZE"]["prefill_kib_per_dispatch"]
+    key = "prefill_bf16_kernel<128, true, false>"
+    out["kernel"] = key
+    out["traffic_bytes_per_launch"] = (f_kib[key] * out["FETCH_SIZE"]["scale"] +
+                                       w_kib[key] * out["WRITE_SIZE"]["scale"]) * 1024.0
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def recorded_traffic():
+    """Bytes per prefill launch from profiles/prefill_traffic.json, or None when the record is
+    missing or was taken on a different prefill kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != prefill_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,7 +201,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run the 1 GiB copy calibration before the timed steps")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/prefill_traffic.json from two rocprofv3 --pmc runs")
+    ap.add_argument("--record-command", default="", help="command line stored with the record")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.record_traffic[0], args.record_traffic[1], args.record_command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -140,6 +224,8 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.pmc_probe:
+        pmc_probe(dev)
     batch = gen.config(5, seed=args.seed)
     nd = batch.num_decodes
     tok0 = int(batch.query_start_loc[nd])
@@ -209,7 +295,11 @@ def main():
         dbytes_l += bl
     floor_s = flops / PEAK_BF16_FLOPS + dbytes_u / PEAK_HBM_BYTES
     value = 100.0 * floor_s / (ms_step / 1e3)
-    achieved = (flops / len(layers)) / (pre_ms_per_launch / 1e3) / 1e12
+    # dominant kernel: the causal prefill launch of layer pass 0
+    pre0_ms = np.mean([e[0][1].elapsed_time(e[0][2]) for e in evs])
+    flops0 = per_pass[0]["prefill_gflop"] * 1e9
+    achieved = flops0 / (pre0_ms / 1e3) / 1e12
+    traffic = recorded_traffic()
     rec = {
         "metric": METRIC, "value": round(value, 3), "unit": "% of roofline",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -226,10 +316,12 @@ def main():
         "decode_gbps_logical": round(dbytes_l / (dec_ms / 1e3) / 1e9, 1),
         "prefill_ms_per_step": round(pre_ms, 4), "decode_ms_per_step": round(dec_ms, 4),
         "per_pass": per_pass,
-        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128,causal>",
+        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128, true, false> "
+                                                  "(causal prefill, layer pass 0)",
+                     "launch_ms": round(pre0_ms, 4), "flop_per_launch": flops0,
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_FLOPS / 1e12,
                      "unit": "TFLOP/s", "frac": round(achieved / (PEAK_BF16_FLOPS / 1e12), 4),
-                     "traffic": None},
+                     "traffic": None if traffic is None else round(traffic)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
