@@ -150,6 +150,7 @@ attn_status attn_varlen_fwd(const attn_desc* desc, const void* q, const void* kv
     dp.max_parts = (int32_t)max_parts;
     dp.window = pp.window;
     dp.scale = scale;
+    dp.group_recip = pp.group_recip;
     if (attn::launch_decode_bf16(dp, st) != hipSuccess) return ATTN_ERR_HIP;
   }
   if (d.num_seqs > d.num_decodes) {

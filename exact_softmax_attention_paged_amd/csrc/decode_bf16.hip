@@ -111,32 +111,40 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
     u32x4 k[2][KC];
     u32x4 v[NV];
   };
-  auto row_off = [&](int key) {
-    const int32_t blk = sBlk[key / p.block_size - b_first];
-    return paged_row(blk, key % p.block_size, kvh, p.block_size, p.num_kv_heads, D);
+  // Element offset of the first row of the 16-key group starting at key g0 (clamped to the
+  // last visible group, so every load below reads a valid row of this request). A 16-key
+  // group lies in one block (block_size is a multiple of 16); the block index comes from
+  // the partition's ids in LDS and the host's 32.32 reciprocal of block_size / 16.
+  const int last_key = k_end - 1;
+  const int last_group = last_key & ~15;
+  const uint32_t block_elems = (uint32_t)(p.block_size * p.num_kv_heads * D);   // < 2^31
+  const int kv_row = p.num_kv_heads * D;
+  auto group_off = [&](int g0, int* first_key) {
+    g0 = min(g0, last_group);
+    *first_key = g0;
+    const uint32_t bidx = (uint32_t)(((uint64_t)(uint32_t)(g0 >> 4) * p.group_recip) >> 32);
+    const int32_t blk = sBlk[bidx - b_first];
+    return (uint64_t)(uint32_t)blk * block_elems +
+           (uint32_t)((g0 - (int)bidx * p.block_size) * kv_row + kvh * D);
   };
+  // keys past the wave's range load a valid row (clamped); their scores are masked, so they
+  // add 0 * (finite V) and need no zeroing
   auto load_chunk = [&](Chunk& ch, int kb) {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
-      const int key = kb + 16 * t2 + li;
-      if (key < k_end) {
-        const int64_t off = row_off(key) + 8 * G;
+      int g0;
+      const uint64_t base = group_off(kb + 16 * t2, &g0);
+      const __bf16* src = kcache + base + (uint32_t)(min(li, last_key - g0) * kv_row + 8 * G);
 #pragma unroll
-        for (int c = 0; c < KC; ++c)
-          ch.k[t2][c] = *reinterpret_cast<const u32x4*>(kcache + off + 32 * c);
-      } else {
-#pragma unroll
-        for (int c = 0; c < KC; ++c) ch.k[t2][c] = u32x4{0, 0, 0, 0};
-      }
+      for (int c = 0; c < KC; ++c) ch.k[t2][c] = *reinterpret_cast<const u32x4*>(src + 32 * c);
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int key = kb + j * RPI + v_row;
-      if (key < k_end) {
-        ch.v[j] = *reinterpret_cast<const u32x4*>(vcache + row_off(key) + 8 * v_chunk);
-      } else {
-        ch.v[j] = u32x4{0, 0, 0, 0};   // past the partition / seq_len: 0 * V stays 0
-      }
+      const int row = j * RPI + v_row;                 // row in the chunk; its 16-key group
+      int g0;                                          // is uniform across the instruction
+      const uint64_t base = group_off(kb + (j * RPI / 16) * 16, &g0);
+      ch.v[j] = *reinterpret_cast<const u32x4*>(
+          vcache + base + (uint32_t)(min(row % 16, last_key - g0) * kv_row + 8 * v_chunk));
     }
   };
 

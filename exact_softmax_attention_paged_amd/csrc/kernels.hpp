@@ -43,6 +43,7 @@ struct DecodeParams {
   int32_t num_decodes, part_tokens, max_parts;  // max_parts: partitions a request may span
   int32_t window;
   float scale;
+  uint64_t group_recip;         // ceil(2^32 / (block_size / 16)), as in PrefillParams
 };
 
 // Partitions of a decode request that hold visible keys: [first, first + count).
