@@ -10,9 +10,10 @@
 // Work split: one workgroup = 8 waves of one (request, q head); each wave owns 32 query rows,
 // one 32-wide MFMA column block, so a workgroup covers 256 rows and every K/V tile brought on
 // chip serves 256 queries. KV is walked in 64-key tiles through two LDS buffers:
-//   * all 512 threads gather the next tile's K and V rows (16-byte loads; the block of each
-//     16-key group is a wave-uniform scalar lookup) into registers while the current tile is
-//     consumed, then store them into the other buffer; one barrier per tile;
+//   * the next tile's K and V rows go from HBM straight into the other buffer
+//     (global_load_lds_dwordx4) while the current tile is consumed: no register staging and
+//     no LDS stores. The block ids of the tile after it are fetched at the same time, so the
+//     addresses are ready when its loads are issued; one barrier per tile;
 //   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, Q^T held in
 //     registers as the B operand). On gfx950 this shape sustains about 1.6x the bf16 rate of
 //     the 16x16x32 shape. Each lane holds 16 keys of one query, so the row max and row sum
@@ -42,6 +43,7 @@ constexpr int kBC = 64;                      // keys per KV tile
 constexpr int kThreads = kWaves * kWave;
 constexpr int kBR = kWaves * kRows;          // query rows per workgroup
 constexpr int kKT = kBC / 32;                // 32-key MFMA tiles per KV tile
+constexpr int kBufs = 2;                     // LDS K/V buffers (prefetch distance 1)
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
@@ -50,19 +52,55 @@ __device__ __forceinline__ floatx16 mfma32x32x16(const bf16x8& a, const bf16x8& 
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// LDS chunk permutation of K/V row r (16-byte chunks; 16 per row for d = 128, 8 for d = 64):
+// the 16 rows read by one half-wave pass of the K operand hit 16 distinct bank groups, and
+// the 4 rows x 4 chunks read by one pass of the transposing V reads are all distinct.
+template <int D>
+__device__ __forceinline__ int swizzle(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Wait for all of this wave's outstanding vector-memory operations (the direct global->LDS
+// loads and the block-id loads of the next tile). gfx9 s_waitcnt: vmcnt 0, expcnt and lgkmcnt
+// left alone.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Workgroup barrier for the K/V buffers, called after wait_vmem(). The memory clobber keeps
+// the compiler from moving memory operations across it; lgkmcnt(0) completes this wave's LDS
+// reads of the tile before another wave may refill its buffer.
+__device__ __forceinline__ void barrier_kv() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Transposing LDS read through a restrict pointer. Inlining a restrict parameter gives the
+// read alias-scope metadata; without it the compiler places a wait for every outstanding
+// direct load (including those filling the other buffer) before each such read.
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+__device__ __attribute__((always_inline)) inline bf16x4 tr_read(
+    const lds_shortx4* __restrict__ ptr) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                        const_cast<lds_shortx4*>(ptr)));
+}
+__device__ __forceinline__ const lds_shortx4* lds_at(uint32_t byte_addr) {
+  return (const lds_shortx4*)(uintptr_t)byte_addr;
+}
+
 template <int D, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const PrefillParams p) {
-  constexpr int RS = D + 16;          // LDS row stride in bf16 (padding against bank conflicts)
   constexpr int KC = D / 16;          // 16-deep k-chunks of the QK^T contraction
   constexpr int DC = D / 32;          // 32-wide d chunks of O^T
-  constexpr int TPR = D / 8;          // threads per K/V row in the gather (16 bytes each)
-  constexpr int RPP = kThreads / TPR;  // rows per gather pass
-  constexpr int NP = kBC / RPP;       // gather passes per tile
-  constexpr int RPW = kWave / TPR;    // rows per wave per pass (4 or 8: divides 16)
-  constexpr int TILE = kBC * RS;
+  constexpr int ROWB = 2 * D;         // bytes per K/V row in LDS (unpadded, swizzled)
+  constexpr int TPR = D / 8;          // lanes per row in a direct load (16 bytes each)
+  constexpr int RPI = kWave / TPR;    // rows per direct-load instruction (4 or 8: divides 16)
+  constexpr int NI = kBC / RPI;       // instructions per K (or V) tile
+  constexpr int IPW = NI / kWaves;    // of them issued by each wave
+  constexpr int TILEB = kBC * ROWB;   // bytes of one K (or V) tile
+  static_assert(IPW * kWaves == NI, "tile rows must split evenly over the waves");
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2 * TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2 * TILE];
+  // [buffer][K, V] tiles, row-major [key][d] with 16-byte chunks XOR-swizzled per row; the
+  // next tile lands in one buffer while the other is consumed
+  __shared__ __attribute__((aligned(1024))) unsigned char sKV[kBufs * 2 * TILEB];
 
   const int r = p.seq_begin + blockIdx.z;
   const int hq = blockIdx.y;
@@ -75,7 +113,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   const int kvh = hq / (p.num_heads / p.num_kv_heads);
 
   const int tid = threadIdx.x;
-  const int w = tid / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave index, uniform
   const int lane = tid % kWave;
   const int h = lane / 32;            // half-wave
   const int lq = lane % 32;           // query column of this lane
@@ -109,60 +147,91 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   const int w_kv_hi = CAUSAL ? min(sl, cl + w_row_hi + 1) : sl;
   const int w_kv_lo = WINDOW ? max(0, cl + w_row_lo - p.window + 1) : 0;
 
-  // ---- gather: thread -> (row in pass, 16-byte chunk). The rows one wave gathers in a pass
-  // lie in one 16-key group, and a 16-key group lies in one cache block (block_size is a
-  // multiple of 16), so the block lookup is wave-uniform: scalar loads of the block table,
-  // one tile ahead of the K/V rows. Block index of group g: g / (block_size / 16), from the
-  // host's 32.32 reciprocal.
-  const int g_row = tid / TPR;
-  const int g_chunk = tid % TPR;
+  // ---- K/V tiles go from HBM straight into LDS (global_load_lds_dwordx4: lane l of one
+  // instruction lands at LDS base + 16 l), so there is no register staging and no LDS store.
+  // An instruction covers RPI consecutive rows; they lie in one 16-key group, which lies in
+  // one cache block (block_size is a multiple of 16), so each instruction needs one block id
+  // (block index of group g: g / (block_size / 16), from the host's 32.32 reciprocal). The
+  // ids of a tile are loaded one tile ahead, lane u holding that of the wave's instruction u,
+  // and read back with v_readlane, so the address arithmetic is scalar. Rows past seq_len
+  // load row seq_len - 1: its scores are masked and 0 * (finite V) adds nothing, so no
+  // zeroing is needed. Because the destination of a lane is fixed, the row layout is
+  // permuted on the source side: LDS chunk slot p of row r holds d-chunk p ^ swz(r), which
+  // keeps both MFMA operand reads free of bank conflicts.
   const uint32_t block_elems = (uint32_t)(p.block_size * p.num_kv_heads * D);   // < 2^31
   const int kv_row = p.num_kv_heads * D;
   const int groups_per_block = p.block_size / 16;
   const int last_group = (sl - 1) >> 4;
-  uint64_t blk_off[NP];     // element offset of the 16-key group each pass reads (uniform)
-  auto fetch_blocks = [&](int tile) {
-    int grp[NP];
-    uint32_t bidx[NP];
-    int32_t blk[NP];
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp) {   // all table loads first, then one wait
-      grp[pp] = min(__builtin_amdgcn_readfirstlane((tile * kBC + pp * RPP + w * RPW) >> 4),
-                    last_group);                     // groups past seq_len: any valid group
-      bidx[pp] = (uint32_t)(((uint64_t)(uint32_t)grp[pp] * p.group_recip) >> 32);
-      blk[pp] = bt[bidx[pp]];
-    }
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp)
-      blk_off[pp] = (uint64_t)(uint32_t)blk[pp] * block_elems +
-                    (uint32_t)((grp[pp] - (int)bidx[pp] * groups_per_block) * 16 * kv_row);
+  const int l_row = lane / TPR;                      // row of this lane within an instruction
+  const int l_slot = lane % TPR;                     // LDS chunk slot of this lane
+  // group index of the first row of direct-load instruction u (u < IPW) of this wave in a tile
+  auto group_of = [&](int tile, int u) {
+    return min((tile * kBC + (w + kWaves * u) * RPI) >> 4, last_group);
   };
-  u32x4 kreg[NP], vreg[NP];
-  auto gather = [&]() {       // K/V rows of the tile whose groups are in blk_off
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp) {
-      const uint32_t lane_off =
-          (uint32_t)((((pp * RPP + w * RPW) & 15) + lane / TPR) * kv_row + kvh * D + g_chunk * 8);
-      kreg[pp] = *reinterpret_cast<const u32x4*>(kcache + blk_off[pp] + lane_off);
-      vreg[pp] = *reinterpret_cast<const u32x4*>(vcache + blk_off[pp] + lane_off);
-    }
+  auto block_index = [&](int grp) {
+    return (uint32_t)(((uint64_t)(uint32_t)grp * p.group_recip) >> 32);
   };
-  auto stash = [&](int buf, int tile) {
-    if (tile * kBC + kBC > sl) {                     // tail tile: zero keys past seq_len
+  // block ids of a tile's IPW instructions: lane u (u < IPW) loads the id of instruction u
+  auto fetch_ids = [&](int tile) {
+    const int u = min(lane, IPW - 1);
+    return bt[block_index(group_of(tile, u))];
+  };
+  // Lane part of the source offset (elements) for tiles that lie wholly below seq_len: row
+  // l_row of the instruction, d-chunk l_slot ^ swizzle(row). The swizzle depends on the row
+  // modulo 16, which is the same for every instruction of this wave (j RPI = w RPI mod 16).
+  const uint32_t lane_src =
+      (uint32_t)(l_row * kv_row + 8 * (l_slot ^ swizzle<D>(w * RPI + l_row)));
+  const uint32_t head_off = (uint32_t)(kvh * D);
+  auto issue_tile = [&](int tile_in, int buf, int32_t ids) {
+    // the tile index is wave-uniform; saying so keeps the address arithmetic scalar
+    const int tile = __builtin_amdgcn_readfirstlane(tile_in);
+    unsigned char* const dst = sKV + buf * (2 * TILEB);
+    const bool full = tile * kBC + kBC <= sl;        // wave-uniform
 #pragma unroll
-      for (int pp = 0; pp < NP; ++pp) {
-        if (tile * kBC + pp * RPP + g_row >= sl) {
-          kreg[pp] = u32x4{0, 0, 0, 0};
-          vreg[pp] = u32x4{0, 0, 0, 0};
-        }
+    for (int u = 0; u < IPW; ++u) {
+      const int j = w + kWaves * u;                  // instruction index within the tile
+      const int32_t blk = __builtin_amdgcn_readlane(ids, u);
+      uint64_t off;
+      if (full) {
+        // rows first .. first + RPI - 1 all lie in the block of group first / 16
+        const int first = tile * kBC + j * RPI;
+        const uint32_t bidx = block_index(first >> 4);
+        off = (uint64_t)(uint32_t)blk * block_elems +
+              (uint32_t)((first - (int)bidx * p.block_size) * kv_row) + head_off + lane_src;
+      } else {
+        // tail tile: rows past seq_len load row seq_len - 1 (its group is the last group)
+        const int grp = __builtin_amdgcn_readfirstlane(group_of(tile, u));
+        const uint32_t bidx = block_index(grp);
+        const int row = j * RPI + l_row;
+        const int key = min(tile * kBC + row, sl - 1);
+        const int slot = (grp - (int)bidx * groups_per_block) * 16 + (key - grp * 16);
+        off = (uint64_t)(uint32_t)blk * block_elems +
+              (uint32_t)(slot * kv_row + head_off + 8 * (l_slot ^ swizzle<D>(row)));
       }
-    }
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp) {
-      *reinterpret_cast<u32x4*>(&sK[buf * TILE + (pp * RPP + g_row) * RS + g_chunk * 8]) = kreg[pp];
-      *reinterpret_cast<u32x4*>(&sV[buf * TILE + (pp * RPP + g_row) * RS + g_chunk * 8]) = vreg[pp];
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(kcache + off),
+          (__attribute__((address_space(3))) void*)(dst + j * (RPI * ROWB)), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(vcache + off),
+          (__attribute__((address_space(3))) void*)(dst + TILEB + j * (RPI * ROWB)), 16, 0, 0);
     }
   };
+
+  // per-lane byte offsets of the transposing V reads within a tile for (kt, g) = (0, 0):
+  // logical column 32dc + 16((lane/16)%2) + 4(lane%4) is 16-byte chunk
+  // 4dc + 2((lane/16)%2) + (lane%4)/2, plus 8 bytes when lane%4 is odd
+  uint32_t v_off0[DC], v_off1[DC];
+  {
+    const int rr = 4 * h + (lane % 16) / 4;
+    const int cchunk = 2 * ((lane / 16) % 2) + (lane % 4) / 2;
+    const int cbyte = 8 * (lane % 2);
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const int ch = 4 * dc + cchunk;
+      v_off0[dc] = rr * ROWB + 16 * (ch ^ swizzle<D>(rr)) + cbyte;
+      v_off1[dc] = (rr + 8) * ROWB + 16 * (ch ^ swizzle<D>(rr + 8)) + cbyte;
+    }
+  }
 
   const float c_log2 = p.scale * kLog2e;
   float m_ref = -INFINITY;
@@ -173,37 +242,53 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[dc][e] = 0.f;
 
+  int32_t ids = 0;
   if (t_begin < t_end) {
-    fetch_blocks(t_begin);
-    gather();
-    if (t_begin + 1 < t_end) fetch_blocks(t_begin + 1);
-    stash(0, t_begin);
+    issue_tile(t_begin, 0, fetch_ids(t_begin));
+    ids = fetch_ids(t_begin + 1);      // clamped to the last group: always a valid entry
   }
-  __syncthreads();
+  wait_vmem();                         // Q, tile t_begin and the ids of tile t_begin + 1
+  barrier_kv();
+  int buf = 0;
   for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
+    // tile t + 1 goes to the other buffer, which every wave finished reading (tile t - 1)
+    // before the barrier that ended the previous iteration
     const bool more = t + 1 < t_end;
-    if (more) {                  // in flight while this tile is consumed
-      gather();
-      if (t + 2 < t_end) fetch_blocks(t + 2);
+    if (more) {
+      issue_tile(t + 1, buf ^ 1, ids);
+      ids = fetch_ids(t + 2);
     }
 
     const int kb = t * kBC;
     if (wave_active && kb < w_kv_hi && kb + kBC > w_kv_lo) {
-      const __bf16* tK = sK + buf * TILE;
-      const __bf16* tV = sV + buf * TILE;
+      const unsigned char* tK = sKV + buf * (2 * TILEB);
+      const unsigned char* tV = tK + TILEB;
       // S^T: sc[kt] element e holds key kb + 32kt + 8(e/4) + 4h + e%4 of query column lq
       floatx16 sc[kKT];
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) {
-        const __bf16* krow = &tK[(kt * 32 + lq) * RS + 8 * h];
-        floatx16 acc;
+      for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+        for (int e = 0; e < 16; ++e) sc[kt][e] = 0.f;
+      {
+        // K row kt*32 + lq has the swizzle of row lq (it depends on the row modulo 16)
+        const int ks = swizzle<D>(lq);
+        const unsigned char* kp = tK + lq * ROWB;
 #pragma unroll
-        for (int c = 0; c < KC; ++c)
-          acc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(krow + 16 * c), qf[c], acc);
-        sc[kt] = acc;
+        for (int c = 0; c < KC; ++c) {
+          const int off = 16 * ((2 * c + h) ^ ks);
+#pragma unroll
+          for (int kt = 0; kt < kKT; ++kt)
+            sc[kt] = mfma32x32x16(
+                *reinterpret_cast<const bf16x8*>(kp + kt * 32 * ROWB + off), qf[c], sc[kt]);
+        }
+        // software pipeline: the K operands of chunk c + 1 are read while chunk c multiplies
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kKT, 0);   // LDS reads
+#pragma unroll
+        for (int c = 0; c + 1 < KC; ++c) {
+          __builtin_amdgcn_sched_group_barrier(0x008, kKT, 0);     // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, kKT, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kKT, 0);
       }
 
       const bool need_mask = (kb + kBC > sl) || (CAUSAL && kb + kBC - 1 > cl + w_row_lo) ||
@@ -252,8 +337,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
 
       // O^T += V^T . P^T, one MFMA per 16 keys: MFMA (kt, g) contracts keys
       // kb + 32kt + 16g + 8(j/4) + 4h + j%4 at k = 8h + j. P^T is elements 8g .. 8g+7 of
-      // sc[kt]; V^T comes from two transposing reads of 4 rows each.
-      const int col0 = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+      // sc[kt]; V^T comes from two transposing reads of 4 rows each (rows r0 and r0 + 8,
+      // r0 = 32kt + 16g + 4h + (lane%16)/4), whose addresses differ from the (kt, g) = (0, 0)
+      // ones by a constant because the swizzle depends on the row modulo 16 only.
+      const uint32_t tv_addr = (uint32_t)(uintptr_t)tV;
+      uint32_t va0[DC], va1[DC];
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        va0[dc] = tv_addr + v_off0[dc];
+        va1[dc] = tv_addr + v_off1[dc];
+      }
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
@@ -263,18 +356,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
           const floatx4 hi = {sc[kt][8 * g + 4], sc[kt][8 * g + 5], sc[kt][8 * g + 6],
                               sc[kt][8 * g + 7]};
           const bf16x8 pb = pack_bf16x8(lo, hi);
-          const int r0 = 32 * kt + 16 * g + 4 * h + (lane % 16) / 4;
+          const uint32_t step = (32 * kt + 16 * g) * ROWB;
 #pragma unroll
           for (int dc = 0; dc < DC; ++dc) {
-            const int col = 32 * dc + col0;
-            const bf16x8 va = concat(lds_read_tr16(&tV[r0 * RS + col]),
-                                     lds_read_tr16(&tV[(r0 + 8) * RS + col]));
+            const bf16x8 va = concat(tr_read(lds_at(va0[dc] + step)),
+                                     tr_read(lds_at(va1[dc] + step)));
             o[dc] = mfma32x32x16(va, pb, o[dc]);
           }
         }
     }
-    if (more) stash(buf ^ 1, t + 1);
-    __syncthreads();
+    wait_vmem();        // this wave's part of tile t + 1 is in LDS ...
+    barrier_kv();       // ... and everyone's, and nobody reads tile t any more
+    buf ^= 1;
   }
 
   // ---- epilogue: O / l and lse = scale * m + ln l
