@@ -22,6 +22,7 @@ ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_METADATA, ATTN_ERR_HIP = 5, 6
 ATTN_BF16, ATTN_F32 = 0, 1
 
 EXPORTED = ("attn_workspace_bytes", "attn_varlen_fwd", "attn_check_metadata_host",
+            "attn_cascade_workspace_bytes", "attn_cascade_fwd", "attn_check_cascade_host",
             "attn_status_str")
 
 
@@ -60,6 +61,13 @@ def lib():
         L.attn_varlen_fwd.restype = i32
         L.attn_check_metadata_host.argtypes = [P(attn_desc), vp, vp, vp]
         L.attn_check_metadata_host.restype = i32
+        L.attn_cascade_workspace_bytes.argtypes = [P(attn_desc), i32, P(sz)]
+        L.attn_cascade_workspace_bytes.restype = i32
+        L.attn_cascade_fwd.argtypes = [P(attn_desc), vp, vp, vp, vp, vp, i32, f32, i32, vp, vp,
+                                       vp, sz, vp]
+        L.attn_cascade_fwd.restype = i32
+        L.attn_check_cascade_host.argtypes = [P(attn_desc), vp, vp, vp, i32]
+        L.attn_check_cascade_host.restype = i32
         L.attn_status_str.argtypes = [i32]
         L.attn_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -122,9 +130,25 @@ def attn_varlen_fwd(desc: attn_desc, q, kv_cache, block_table, query_start_loc, 
     [2, num_blocks, block_size, Hkv, d] (bf16 or f32 as desc.dtype), int32 metadata, fp32 lse
     (or None) and a uint8 workspace of attn_workspace_bytes(desc) bytes (or None if 0)."""
     import torch
+    _check_call("attn_varlen_fwd", desc, q, kv_cache, block_table, query_start_loc, seq_lens,
+                out, lse, workspace)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib().attn_varlen_fwd(ctypes.byref(desc), _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                               _ptr(query_start_loc), _ptr(seq_lens), float(scale),
+                               1 if causal else 0, int(window), _ptr(out), _ptr(lse),
+                               _ptr(workspace), ws_bytes, ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_varlen_fwd")
+
+
+def _check_call(where, desc, q, kv_cache, block_table, query_start_loc, seq_lens, out, lse,
+                workspace):
+    import torch
     dev = q.device
     if dev.type != "cuda":
-        raise ValueError("attn_varlen_fwd runs on a GPU device; q is on " + str(dev))
+        raise ValueError(where + " runs on a GPU device; q is on " + str(dev))
     dt = torch.bfloat16 if desc.dtype == ATTN_BF16 else torch.float32
     _check_tensor("q", q, dt, dev)
     _check_tensor("kv_cache", kv_cache, dt, dev)
@@ -141,15 +165,46 @@ def attn_varlen_fwd(desc: attn_desc, q, kv_cache, block_table, query_start_loc, 
     if tuple(kv_cache.shape) != (2, desc.num_blocks, desc.block_size, desc.num_kv_heads,
                                  desc.head_size):
         raise ValueError("kv_cache shape does not match desc")
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    ws_bytes = 0 if workspace is None else workspace.numel()
-    st = lib().attn_varlen_fwd(ctypes.byref(desc), _ptr(q), _ptr(kv_cache), _ptr(block_table),
-                               _ptr(query_start_loc), _ptr(seq_lens), float(scale),
-                               1 if causal else 0, int(window), _ptr(out), _ptr(lse),
-                               _ptr(workspace), ws_bytes, ctypes.c_void_p(stream.cuda_stream))
+
+
+def attn_cascade_workspace_bytes(desc: attn_desc, common_prefix_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().attn_cascade_workspace_bytes(ctypes.byref(desc), int(common_prefix_len),
+                                            ctypes.byref(n))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_varlen_fwd")
+        raise AttnError(st, "attn_cascade_workspace_bytes")
+    return int(n.value)
+
+
+def attn_check_cascade_host(desc: attn_desc, block_table: np.ndarray,
+                            query_start_loc: np.ndarray, seq_lens: np.ndarray,
+                            common_prefix_len: int) -> int:
+    """Returns the status code of the host-side cascade precondition check."""
+    arrs = [np.ascontiguousarray(a, dtype=np.int32) for a in (block_table, query_start_loc,
+                                                               seq_lens)]
+    ptrs = [a.ctypes.data_as(ctypes.c_void_p) for a in arrs]
+    return int(lib().attn_check_cascade_host(ctypes.byref(desc), *ptrs, int(common_prefix_len)))
+
+
+def attn_cascade_fwd(desc: attn_desc, q, kv_cache, block_table, query_start_loc, seq_lens,
+                     common_prefix_len: int, scale: float, causal: bool, out, lse, workspace,
+                     stream=None) -> None:
+    """Queue a cascade attention call (shared prefix computed once; see include/attn.h).
+
+    Tensors as for attn_varlen_fwd; the workspace holds
+    attn_cascade_workspace_bytes(desc, common_prefix_len) bytes."""
+    import torch
+    _check_call("attn_cascade_fwd", desc, q, kv_cache, block_table, query_start_loc, seq_lens,
+                out, lse, workspace)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib().attn_cascade_fwd(ctypes.byref(desc), _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                                _ptr(query_start_loc), _ptr(seq_lens), int(common_prefix_len),
+                                float(scale), 1 if causal else 0, _ptr(out), _ptr(lse),
+                                _ptr(workspace), ws_bytes, ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_cascade_fwd")
 
 
 def varlen_fwd(q, kv_cache, block_table, query_start_loc, seq_lens, *, scale, causal, window=0,

@@ -63,6 +63,81 @@ size_t workspace_for(const attn_desc* d, int64_t max_parts) {
   return (size_t)ceil_div(floats * 4, 256) * 256;
 }
 
+size_t round256(int64_t bytes) { return (size_t)ceil_div(bytes, 256) * 256; }
+
+// Cascade workspace: the prefix pass's fp32 partial result for every query row
+// ([num_tokens][Hq][d], then [num_tokens][Hq] log-sum-exps), followed by the decode
+// partitions' workspace of the suffix pass.
+size_t cascade_prefix_bytes(const attn_desc* d) {
+  const int64_t rows = (int64_t)d->num_tokens * d->num_heads;
+  return round256(rows * d->head_size * 4) + round256(rows * 4);
+}
+
+attn::PrefillParams prefill_params(const attn_desc& d, const void* q, const void* kv_cache,
+                                   const int32_t* block_table, const int32_t* qsl,
+                                   const int32_t* seq_lens, float scale, int32_t causal,
+                                   int32_t window, void* out, float* lse) {
+  attn::PrefillParams pp{};
+  pp.q = q;
+  pp.kv = kv_cache;
+  pp.block_table = block_table;
+  pp.qsl = qsl;
+  pp.seq_lens = seq_lens;
+  pp.out = out;
+  pp.lse = lse;
+  pp.v_offset = (int64_t)d.num_blocks * d.block_size * d.num_kv_heads * d.head_size;
+  pp.num_heads = d.num_heads;
+  pp.num_kv_heads = d.num_kv_heads;
+  pp.head_size = d.head_size;
+  pp.block_size = d.block_size;
+  pp.max_blocks = d.max_blocks_per_seq;
+  pp.max_query_len = d.max_query_len;
+  pp.causal = causal ? 1 : 0;
+  pp.window = window > 0 ? window : 0;
+  pp.scale = scale;
+  const uint64_t groups = (uint64_t)(d.block_size / 16);
+  pp.group_recip = (((uint64_t)1 << 32) + groups - 1) / groups;
+  return pp;
+}
+
+attn::DecodeParams decode_params(const attn_desc& d, const attn::PrefillParams& pp,
+                                 int64_t max_parts, float* ws) {
+  attn::DecodeParams dp{};
+  dp.q = pp.q;
+  dp.kv = pp.kv;
+  dp.block_table = pp.block_table;
+  dp.qsl = pp.qsl;
+  dp.seq_lens = pp.seq_lens;
+  dp.out = pp.out;
+  dp.lse = pp.lse;
+  dp.ws_o = ws;
+  dp.ws_lse = ws + (int64_t)d.num_decodes * d.num_heads * max_parts * d.head_size;
+  dp.v_offset = pp.v_offset;
+  dp.num_heads = d.num_heads;
+  dp.num_kv_heads = d.num_kv_heads;
+  dp.head_size = d.head_size;
+  dp.block_size = d.block_size;
+  dp.max_blocks = d.max_blocks_per_seq;
+  dp.num_decodes = d.num_decodes;
+  dp.part_tokens = partition_tokens(&d);
+  dp.max_parts = (int32_t)max_parts;
+  dp.window = pp.window;
+  dp.scale = pp.scale;
+  dp.group_recip = pp.group_recip;
+  return dp;
+}
+
+// Checks of a cascade call that need nothing but the descriptor and the prefix length.
+attn_status check_cascade(const attn_desc* d, int32_t common_prefix_len) {
+  const attn_status s = check_desc(d);
+  if (s != ATTN_OK) return s;
+  if (d->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (common_prefix_len < 0 || common_prefix_len % d->block_size != 0 ||
+      common_prefix_len > d->max_seq_len)
+    return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -95,68 +170,110 @@ attn_status attn_varlen_fwd(const attn_desc* desc, const void* q, const void* kv
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int64_t v_offset = (int64_t)d.num_blocks * d.block_size * d.num_kv_heads * d.head_size;
-
-  attn::PrefillParams pp{};
-  pp.q = q;
-  pp.kv = kv_cache;
-  pp.block_table = block_table;
-  pp.qsl = query_start_loc;
-  pp.seq_lens = seq_lens;
-  pp.out = out;
-  pp.lse = lse;
-  pp.v_offset = v_offset;
-  pp.num_heads = d.num_heads;
-  pp.num_kv_heads = d.num_kv_heads;
-  pp.head_size = d.head_size;
-  pp.block_size = d.block_size;
-  pp.max_blocks = d.max_blocks_per_seq;
-  pp.max_query_len = d.max_query_len;
-  pp.causal = causal ? 1 : 0;
-  pp.window = window > 0 ? window : 0;
-  pp.scale = scale;
-  {
-    const uint64_t groups = (uint64_t)(d.block_size / 16);
-    pp.group_recip = (((uint64_t)1 << 32) + groups - 1) / groups;
-  }
-
+  attn::PrefillParams pp = prefill_params(d, q, kv_cache, block_table, query_start_loc,
+                                          seq_lens, scale, causal, window, out, lse);
   if (d.dtype == ATTN_F32) {
     // float32 runs every request, decode rows included, through the fp32 prefill kernel
     pp.seq_begin = 0;
     pp.num_seqs = d.num_seqs;
     return attn::launch_prefill_f32(pp, st) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
   }
-
   if (d.num_decodes > 0) {
-    attn::DecodeParams dp{};
-    dp.q = q;
-    dp.kv = kv_cache;
-    dp.block_table = block_table;
-    dp.qsl = query_start_loc;
-    dp.seq_lens = seq_lens;
-    dp.out = out;
-    dp.lse = lse;
-    dp.ws_o = static_cast<float*>(workspace);
-    dp.ws_lse = static_cast<float*>(workspace) +
-                (int64_t)d.num_decodes * d.num_heads * max_parts * d.head_size;
-    dp.v_offset = v_offset;
-    dp.num_heads = d.num_heads;
-    dp.num_kv_heads = d.num_kv_heads;
-    dp.head_size = d.head_size;
-    dp.block_size = d.block_size;
-    dp.max_blocks = d.max_blocks_per_seq;
-    dp.num_decodes = d.num_decodes;
-    dp.part_tokens = partition_tokens(&d);
-    dp.max_parts = (int32_t)max_parts;
-    dp.window = pp.window;
-    dp.scale = scale;
-    dp.group_recip = pp.group_recip;
+    const attn::DecodeParams dp =
+        decode_params(d, pp, max_parts, static_cast<float*>(workspace));
     if (attn::launch_decode_bf16(dp, st) != hipSuccess) return ATTN_ERR_HIP;
   }
   if (d.num_seqs > d.num_decodes) {
     pp.seq_begin = d.num_decodes;
     pp.num_seqs = d.num_seqs - d.num_decodes;
     if (attn::launch_prefill_bf16(pp, st) != hipSuccess) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+attn_status attn_cascade_workspace_bytes(const attn_desc* desc, int32_t common_prefix_len,
+                                         size_t* bytes) {
+  if (bytes == nullptr) return ATTN_ERR_NULL;
+  const attn_status s = check_cascade(desc, common_prefix_len);
+  if (s != ATTN_OK) return s;
+  const size_t suffix = workspace_for(desc, decode_max_parts(desc, 0));
+  *bytes = common_prefix_len == 0 ? suffix : cascade_prefix_bytes(desc) + suffix;
+  return ATTN_OK;
+}
+
+attn_status attn_cascade_fwd(const attn_desc* desc, const void* q, const void* kv_cache,
+                             const int32_t* block_table, const int32_t* query_start_loc,
+                             const int32_t* seq_lens, int32_t common_prefix_len, float scale,
+                             int32_t causal, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  attn_status s = check_cascade(desc, common_prefix_len);
+  if (s != ATTN_OK) return s;
+  if (common_prefix_len == 0)
+    return attn_varlen_fwd(desc, q, kv_cache, block_table, query_start_loc, seq_lens, scale,
+                           causal, 0, out, lse, workspace, workspace_bytes, stream);
+  const attn_desc& d = *desc;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (d.num_seqs == 0 || d.num_tokens == 0) return ATTN_OK;
+  if (q == nullptr || kv_cache == nullptr || block_table == nullptr ||
+      query_start_loc == nullptr || seq_lens == nullptr || out == nullptr)
+    return ATTN_ERR_NULL;
+  const int64_t max_parts = decode_max_parts(&d, 0);
+  const size_t pre_bytes = cascade_prefix_bytes(&d);
+  const size_t need = pre_bytes + workspace_for(&d, max_parts);
+  if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* pre_o = static_cast<float*>(workspace);
+  float* pre_lse = pre_o + round256((int64_t)d.num_tokens * d.num_heads * d.head_size * 4) / 4;
+  float* ws_suffix = reinterpret_cast<float*>(static_cast<char*>(workspace) + pre_bytes);
+  const int32_t skip = common_prefix_len / d.block_size;
+
+  // 1. prefix pass: every query token of the batch against the shared prefix, no mask
+  attn::PrefillParams pre = prefill_params(d, q, kv_cache, block_table, query_start_loc,
+                                           seq_lens, scale, 0, 0, nullptr, pre_lse);
+  pre.single_ql = d.num_tokens;
+  pre.single_sl = common_prefix_len;
+  pre.max_query_len = d.num_tokens;
+  pre.num_seqs = 1;
+  pre.out_f32 = pre_o;
+  if (attn::launch_prefill_bf16(pre, st) != hipSuccess) return ATTN_ERR_HIP;
+
+  // 2. suffix pass over the keys after the prefix, merged with the prefix result
+  attn::PrefillParams pp = prefill_params(d, q, kv_cache, block_table, query_start_loc,
+                                          seq_lens, scale, causal, 0, out, lse);
+  pp.kv_skip_blocks = skip;
+  if (d.num_decodes > 0) {
+    attn::DecodeParams dp = decode_params(d, pp, max_parts, ws_suffix);
+    dp.kv_skip_blocks = skip;
+    dp.pre_o = pre_o;
+    dp.pre_lse = pre_lse;
+    if (attn::launch_decode_bf16(dp, st) != hipSuccess) return ATTN_ERR_HIP;
+  }
+  if (d.num_seqs > d.num_decodes) {
+    pp.seq_begin = d.num_decodes;
+    pp.num_seqs = d.num_seqs - d.num_decodes;
+    pp.init_o = pre_o;
+    pp.init_lse = pre_lse;
+    if (attn::launch_prefill_bf16(pp, st) != hipSuccess) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+attn_status attn_check_cascade_host(const attn_desc* desc, const int32_t* block_table,
+                                    const int32_t* query_start_loc, const int32_t* seq_lens,
+                                    int32_t common_prefix_len) {
+  attn_status s = check_cascade(desc, common_prefix_len);
+  if (s != ATTN_OK) return s;
+  s = attn_check_metadata_host(desc, block_table, query_start_loc, seq_lens);
+  if (s != ATTN_OK) return s;
+  const attn_desc& d = *desc;
+  const int64_t nb = common_prefix_len / d.block_size;
+  for (int32_t r = 0; r < d.num_seqs; ++r) {
+    const int64_t ql = (int64_t)query_start_loc[r + 1] - query_start_loc[r];
+    if ((int64_t)seq_lens[r] - ql < common_prefix_len) return ATTN_ERR_METADATA;
+    for (int64_t b = 0; b < nb; ++b)
+      if (block_table[(int64_t)r * d.max_blocks_per_seq + b] != block_table[b])
+        return ATTN_ERR_METADATA;
   }
   return ATTN_OK;
 }

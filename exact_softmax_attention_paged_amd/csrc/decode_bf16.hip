@@ -54,7 +54,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   const int nh = min(16, group - hg * 16);             // q heads in this workgroup
   const int h0 = kvh * group + hg * 16;                // first q head
 
-  const int sl = p.seq_lens[r];
+  // keys of this pass: [0, sl) after skipping kv_skip_blocks leading blocks
+  const int sl = p.seq_lens[r] - p.kv_skip_blocks * p.block_size;
   int first, nparts;
   decode_partitions(sl, p.window, p.part_tokens, &first, &nparts);
   nparts = min(nparts, p.max_parts);   // only reachable with seq_len > max_seq_len
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   // block ids covering [p_start, k_end) -> LDS, so the K/V loads need no dependent lookup
   const int b_first = p_start / p.block_size;
   const int n_blk = (k_end - 1) / p.block_size - b_first + 1;
-  const int32_t* __restrict__ bt = p.block_table + (int64_t)r * p.max_blocks;
+  const int32_t* __restrict__ bt = p.block_table + (int64_t)r * p.max_blocks + p.kv_skip_blocks;
   for (int i = tid; i < n_blk; i += 256) sBlk[i] = bt[b_first + i];
 
   const __bf16* __restrict__ q = static_cast<const __bf16*>(p.q);
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   }
   const float lse_part = L > 0.f ? p.scale * M + __logf(L) : -INFINITY;
   const int hq = h0 + hh;
-  if (nparts == 1) {
+  if (nparts == 1 && p.pre_o == nullptr) {
     __bf16* dst = static_cast<__bf16*>(p.out) + ((int64_t)tok * p.num_heads + hq) * D + d0;
 #pragma unroll
     for (int x = 0; x < DPT; ++x) dst[x] = to_bf16(acc[x]);
@@ -276,19 +277,24 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   }
 }
 
-// One wave per (q head, decode request): out = sum_p exp(lse_p - L) o_p, lse = L.
+// One wave per (q head, decode request): out = sum_p exp(lse_p - L) o_p, lse = L, over the
+// request's partitions plus, in a cascade suffix pass, the prefix's partial result.
 template <int D>
 __global__ __launch_bounds__(64) void lse_merge_kernel(const DecodeParams p) {
   const int hq = blockIdx.x;
   const int r = blockIdx.y;
-  const int sl = p.seq_lens[r];
+  const int sl = p.seq_lens[r] - p.kv_skip_blocks * p.block_size;
   int first, nparts;
   decode_partitions(sl, p.window, p.part_tokens, &first, &nparts);
   nparts = min(nparts, p.max_parts);
-  if (nparts <= 1) return;        // written directly by the split kernel
+  const bool pre = p.pre_o != nullptr;
+  if (nparts <= 1 && !pre) return;        // written directly by the split kernel
   const int lane = threadIdx.x;
+  const int tok = p.qsl[r];
   const int64_t base = ((int64_t)r * p.num_heads + hq) * p.max_parts;
-  float M = -INFINITY;
+  const int64_t row = (int64_t)tok * p.num_heads + hq;
+  const float lse_pre = pre ? p.pre_lse[row] : -INFINITY;
+  float M = lse_pre;
   for (int pi = lane; pi < nparts; pi += kWave) M = fmaxf(M, p.ws_lse[base + pi]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
@@ -297,6 +303,7 @@ __global__ __launch_bounds__(64) void lse_merge_kernel(const DecodeParams p) {
   for (int pi = lane; pi < nparts; pi += kWave) S += fast_exp2((p.ws_lse[base + pi] - M_use) * kLog2e);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
+  S += fast_exp2((lse_pre - M_use) * kLog2e);          // 0 without a prefix
   const float L = S > 0.f ? M_use + __logf(S) : -INFINITY;
   constexpr int DPL = D / kWave;
   float acc[DPL];
@@ -308,11 +315,16 @@ __global__ __launch_bounds__(64) void lse_merge_kernel(const DecodeParams p) {
 #pragma unroll
     for (int x = 0; x < DPL; ++x) acc[x] += wgt * src[lane + kWave * x];
   }
-  const int tok = p.qsl[r];
-  __bf16* dst = static_cast<__bf16*>(p.out) + ((int64_t)tok * p.num_heads + hq) * D;
+  if (pre && S > 0.f) {
+    const float wgt = fast_exp2((lse_pre - L) * kLog2e);
+    const float* src = p.pre_o + row * D;
+#pragma unroll
+    for (int x = 0; x < DPL; ++x) acc[x] += wgt * src[lane + kWave * x];
+  }
+  __bf16* dst = static_cast<__bf16*>(p.out) + row * D;
 #pragma unroll
   for (int x = 0; x < DPL; ++x) dst[lane + kWave * x] = to_bf16(acc[x]);
-  if (p.lse != nullptr && lane == 0) p.lse[(int64_t)tok * p.num_heads + hq] = L;
+  if (p.lse != nullptr && lane == 0) p.lse[row] = L;
 }
 
 template <int D>
@@ -322,7 +334,7 @@ hipError_t launch(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.num_kv_heads * head_groups, p.max_parts, p.num_decodes);
   hipLaunchKernelGGL(decode_split_kernel<D>, grid, dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.max_parts <= 1) return e;
+  if (e != hipSuccess || (p.max_parts <= 1 && p.pre_o == nullptr)) return e;
   hipLaunchKernelGGL(lse_merge_kernel<D>, dim3(p.num_heads, p.num_decodes), dim3(kWave), 0,
                      stream, p);
   return hipGetLastError();

@@ -25,6 +25,15 @@ struct PrefillParams {
   float scale;
   uint64_t group_recip;         // ceil(2^32 / (block_size / 16)): block index of key k is
                                 // ((k / 16) * group_recip) >> 32 for k * block_size < 2^40
+  // Cascade passes (all zero / null for a plain call):
+  int32_t kv_skip_blocks;       // keys start after this many blocks of every request (the
+                                // shared prefix); seq_len shrinks by kv_skip_blocks*block_size
+  int32_t single_ql, single_sl; // single_ql > 0: one sequence whose queries are rows
+                                // [0, single_ql) of q and whose keys are the first single_sl
+                                // keys of block-table row 0 (the prefix pass)
+  float* out_f32;               // non-null: write O (normalised) in fp32 here, not to out
+  const float* init_o;          // non-null: start each row from a partial result over
+  const float* init_lse;        // earlier keys, fp32 [token][head][d] and [token][head]
 };
 
 // One split-KV decode launch covers requests [0, num_decodes): each has query_len == 1.
@@ -44,6 +53,11 @@ struct DecodeParams {
   int32_t window;
   float scale;
   uint64_t group_recip;         // ceil(2^32 / (block_size / 16)), as in PrefillParams
+  // Cascade suffix pass (zero / null for a plain call):
+  int32_t kv_skip_blocks;       // as in PrefillParams
+  const float* pre_o;           // non-null: a partial result over the prefix, fp32
+  const float* pre_lse;         // [token][head][d] and [token][head], merged as one more
+                                // partition (every row then goes through the merge kernel)
 };
 
 // Partitions of a decode request that hold visible keys: [first, first + count).

@@ -102,13 +102,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   // next tile lands in one buffer while the other is consumed
   __shared__ __attribute__((aligned(1024))) unsigned char sKV[kBufs * 2 * TILEB];
 
-  const int r = p.seq_begin + blockIdx.z;
+  const bool single = p.single_ql > 0;          // cascade prefix pass: one sequence
+  const int r = single ? 0 : p.seq_begin + blockIdx.z;
   const int hq = blockIdx.y;
   const int qt = gridDim.x - 1 - blockIdx.x;   // longest (causal) tiles are dispatched first
-  const int q_start = p.qsl[r];
-  const int ql = p.qsl[r + 1] - q_start;
+  const int q_start = single ? 0 : p.qsl[r];
+  const int ql = single ? p.single_ql : p.qsl[r + 1] - q_start;
   if (qt * kBR >= ql) return;
-  const int sl = p.seq_lens[r];
+  // keys of this pass: [0, sl) after skipping kv_skip_blocks leading blocks
+  const int sl = single ? p.single_sl : p.seq_lens[r] - p.kv_skip_blocks * p.block_size;
   const int cl = sl - ql;
   const int kvh = hq / (p.num_heads / p.num_kv_heads);
 
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   const __bf16* __restrict__ q = static_cast<const __bf16*>(p.q);
   const __bf16* __restrict__ kcache = static_cast<const __bf16*>(p.kv);
   const __bf16* __restrict__ vcache = kcache + p.v_offset;
-  const int32_t* __restrict__ bt = p.block_table + (int64_t)r * p.max_blocks;
+  const int32_t* __restrict__ bt = p.block_table + (int64_t)r * p.max_blocks + p.kv_skip_blocks;
   const int64_t row_stride = (int64_t)p.num_heads * D;   // q/out stride between tokens
 
   // ---- Q^T (B operand): lane l holds query lq, d = 16c + 8h .. +7
@@ -241,6 +243,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[dc][e] = 0.f;
+
+  // A partial result over earlier keys (out o0 normalised, log-sum-exp lse0) is the state
+  // O = o0, l = 1 with the reference max m = lse0 / scale: the prefix's sum of
+  // exp(scale (s - m)) is exp(lse0 - scale m) = 1.
+  if (p.init_o != nullptr) {
+    const int64_t ri = (int64_t)(q_start + min(wrow0 + lq, ql - 1)) * p.num_heads + hq;
+    const float lse0 = p.init_lse[ri];
+    if (lse0 > -INFINITY) {
+      m_ref = lse0 / p.scale;
+      l_run = h == 0 ? 1.f : 0.f;                // the lane pair's partial sums add up to 1
+      const float* src = p.init_o + ri * D + 4 * h;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const floatx4 v = *reinterpret_cast<const floatx4*>(src + 32 * dc + 8 * e4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[dc][4 * e4 + i] = v[i];
+        }
+    }
+  }
 
   int32_t ids = 0;
   if (t_begin < t_end) {
@@ -375,19 +398,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   const int row = wrow0 + lq;
   if (row < ql) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* dst = static_cast<__bf16*>(p.out) + (int64_t)(q_start + row) * row_stride +
-                  (int64_t)hq * D + 4 * h;
+    const int64_t off = (int64_t)(q_start + row) * row_stride + (int64_t)hq * D + 4 * h;
+    if (p.out_f32 != nullptr) {
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc)
+      for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        bf16x4 v;
-        v[0] = to_bf16(o[dc][4 * e4 + 0] * inv);
-        v[1] = to_bf16(o[dc][4 * e4 + 1] * inv);
-        v[2] = to_bf16(o[dc][4 * e4 + 2] * inv);
-        v[3] = to_bf16(o[dc][4 * e4 + 3] * inv);
-        *reinterpret_cast<bf16x4*>(dst + 32 * dc + 8 * e4) = v;
-      }
+        for (int e4 = 0; e4 < 4; ++e4)
+          *reinterpret_cast<floatx4*>(p.out_f32 + off + 32 * dc + 8 * e4) =
+              floatx4{o[dc][4 * e4 + 0] * inv, o[dc][4 * e4 + 1] * inv,
+                      o[dc][4 * e4 + 2] * inv, o[dc][4 * e4 + 3] * inv};
+    } else {
+      __bf16* dst = static_cast<__bf16*>(p.out) + off;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          bf16x4 v;
+          v[0] = to_bf16(o[dc][4 * e4 + 0] * inv);
+          v[1] = to_bf16(o[dc][4 * e4 + 1] * inv);
+          v[2] = to_bf16(o[dc][4 * e4 + 2] * inv);
+          v[3] = to_bf16(o[dc][4 * e4 + 3] * inv);
+          *reinterpret_cast<bf16x4*>(dst + 32 * dc + 8 * e4) = v;
+        }
+    }
     if (p.lse != nullptr && h == 0) {
       p.lse[(int64_t)(q_start + row) * p.num_heads + hq] =
           l_tot > 0.f ? p.scale * m_ref + __logf(l_tot) : -INFINITY;

@@ -153,6 +153,53 @@ attn_status attn_varlen_fwd(const attn_desc* desc, const void* q, const void* kv
 attn_status attn_check_metadata_host(const attn_desc* desc, const int32_t* block_table,
                                      const int32_t* query_start_loc, const int32_t* seq_lens);
 
+/*
+ * Cascade attention for a prefix shared by every request of the batch ([FA] "Cascade
+ * Attention: 공통 프리픽스 최적화" section, and the use_cascade / common_prefix_len fields of
+ * its FlashAttentionMetadata section). The result is the same exact attention as
+ * attn_varlen_fwd with window = 0; it is computed as
+ *   1. a prefix pass: one sequence whose queries are all num_tokens query rows and whose keys
+ *      are the first common_prefix_len keys (read through block_table row 0), not causal,
+ *      written as fp32 partial results to the workspace;
+ *   2. a suffix pass: every request over its keys [common_prefix_len, seq_len), causal when
+ *      `causal` is set, merged with the prefix result through the log-sum-exps ([RBLN]
+ *      Overview: partial softmax results combined) - inside the prefill kernel for prefill
+ *      rows, in the partition merge kernel for decode rows.
+ * The prefix K/V are read once per kv head for the whole batch instead of once per request.
+ *
+ * Preconditions (trusted on the device; attn_check_cascade_host checks host copies):
+ *   common_prefix_len is a multiple of block_size; the first common_prefix_len / block_size
+ *   block-table entries are the same for every request; every request's context length
+ *   seq_len - query_len is >= common_prefix_len (each query sits after the prefix).
+ * common_prefix_len == 0 is a plain attn_varlen_fwd call (window 0).
+ *
+ * attn_cascade_workspace_bytes: bytes of device workspace attn_cascade_fwd needs:
+ *   num_tokens * num_heads * (head_size + 1) * 4 bytes (each part rounded up to 256) for the
+ *   prefix result, plus attn_workspace_bytes(desc) for the decode partitions;
+ *   attn_workspace_bytes(desc) alone when common_prefix_len == 0.
+ * attn_cascade_fwd: arguments as attn_varlen_fwd (no window), plus common_prefix_len.
+ * Errors: those of attn_varlen_fwd; ATTN_ERR_UNSUPPORTED for a dtype other than ATTN_BF16;
+ * ATTN_ERR_SHAPE when common_prefix_len is negative, not a multiple of block_size or larger
+ * than max_seq_len; ATTN_ERR_WORKSPACE when workspace_bytes is below
+ * attn_cascade_workspace_bytes.
+ */
+attn_status attn_cascade_workspace_bytes(const attn_desc* desc, int32_t common_prefix_len,
+                                         size_t* bytes);
+attn_status attn_cascade_fwd(const attn_desc* desc, const void* q, const void* kv_cache,
+                             const int32_t* block_table, const int32_t* query_start_loc,
+                             const int32_t* seq_lens, int32_t common_prefix_len, float scale,
+                             int32_t causal, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * attn_check_cascade_host: attn_check_metadata_host plus the cascade preconditions above
+ * (shared prefix blocks, every context length >= common_prefix_len), on host copies.
+ * Returns ATTN_OK, ATTN_ERR_METADATA, or the descriptor errors of attn_cascade_fwd.
+ */
+attn_status attn_check_cascade_host(const attn_desc* desc, const int32_t* block_table,
+                                    const int32_t* query_start_loc, const int32_t* seq_lens,
+                                    int32_t common_prefix_len);
+
 /* attn_status_str: static, NUL-terminated name of a status code ("ATTN_OK", ...). */
 const char* attn_status_str(int32_t status);
 

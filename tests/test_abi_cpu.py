@@ -155,3 +155,59 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(5, 8, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         A.attn_varlen_fwd(_desc(), q, q, q, q, q, 0.1, True, 0, q, None, None)
+
+
+# ---------------------------------------------------------------- cascade entry points
+def _cascade(desc, prefix, causal=1, scale=0.125, ws=None, ws_bytes=0, q=FAKE, out=FAKE):
+    return A.lib().attn_cascade_fwd(ctypes.byref(desc), q, FAKE, FAKE, FAKE, FAKE, prefix,
+                                    scale, causal, out, None, ws, ws_bytes, None)
+
+
+def test_cascade_argument_errors():
+    d = _desc()
+    assert _cascade(d, -16) == A.ATTN_ERR_SHAPE
+    assert _cascade(d, 8) == A.ATTN_ERR_SHAPE                    # not a whole block
+    assert _cascade(d, 48) == A.ATTN_ERR_SHAPE                   # beyond max_seq_len
+    assert _cascade(_desc(dtype=A.ATTN_F32), 16) == A.ATTN_ERR_UNSUPPORTED
+    assert _cascade(_desc(block_size=24), 16) == A.ATTN_ERR_BLOCK_SIZE
+    assert _cascade(d, 16, scale=0.0) == A.ATTN_ERR_UNSUPPORTED
+    assert _cascade(d, 16, q=None) == A.ATTN_ERR_NULL
+    need = A.attn_cascade_workspace_bytes(d, 16)
+    assert _cascade(d, 16, ws=None) == A.ATTN_ERR_WORKSPACE
+    assert _cascade(d, 16, ws=FAKE, ws_bytes=need - 1) == A.ATTN_ERR_WORKSPACE
+    n = ctypes.c_size_t(0)
+    assert A.lib().attn_cascade_workspace_bytes(ctypes.byref(d), 16, None) == A.ATTN_ERR_NULL
+    assert A.lib().attn_cascade_workspace_bytes(ctypes.byref(d), 8, ctypes.byref(n)) == \
+        A.ATTN_ERR_SHAPE
+
+
+def test_cascade_workspace_size():
+    d = _desc(num_decodes=1, max_seq_len=40)
+    plain = A.attn_workspace_bytes(d)
+    assert A.attn_cascade_workspace_bytes(d, 0) == plain
+    rows = 5 * 8                                              # num_tokens x num_heads
+    pre = -(-(rows * 128 * 4) // 256) * 256 + -(-(rows * 4) // 256) * 256
+    assert A.attn_cascade_workspace_bytes(d, 16) == pre + plain
+    assert A.attn_cascade_workspace_bytes(_desc(num_decodes=0), 32) == pre
+
+
+def test_cascade_checker():
+    d = _desc()
+    qsl = np.array([0, 1, 5], np.int32)
+    sl = np.array([17, 40], np.int32)                          # contexts 16 and 36
+    bt = np.array([[3, 4, 7], [3, 1, 2]], np.int32)            # block 3 shared
+    assert A.attn_check_cascade_host(d, bt, qsl, sl, 16) == A.ATTN_OK
+    assert A.attn_check_cascade_host(d, bt, qsl, sl, 0) == A.ATTN_OK
+    assert A.attn_check_cascade_host(d, bt, qsl, sl, 32) == A.ATTN_ERR_METADATA   # 2nd block differs
+    b = bt.copy(); b[1, 0] = 5
+    assert A.attn_check_cascade_host(d, b, qsl, sl, 16) == A.ATTN_ERR_METADATA    # prefix not shared
+    assert A.attn_check_cascade_host(d, bt, qsl, np.array([15, 40], np.int32), 16) == \
+        A.ATTN_ERR_METADATA                                    # context 14 < prefix 16
+    assert A.attn_check_cascade_host(d, bt, qsl, sl, 8) == A.ATTN_ERR_SHAPE
+
+
+def test_cascade_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(5, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        A.attn_cascade_fwd(_desc(), q, q, q, q, q, 16, 0.1, True, q, None, None)

@@ -53,7 +53,7 @@ def test_small_batches_match_oracle(name, kw, causal, window):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 300)])
 def test_large_prefill_matches_oracle(d, causal, window):
-    """Enough query tiles that the prefill kernel takes its 64-rows-per-wave variant."""
+    """Several 256-row query tiles per request, ragged ends, GQA 4."""
     b = _batch(11, ql=[1024, 1000, 777, 1024], sl=[1024, 1300, 2000, 1100], hq=32, hkv=8, d=d,
                bs=32)
     print(f"[case] large prefill d={d} causal={causal} window={window}", flush=True)
