@@ -194,6 +194,71 @@ def recorded_traffic():
     return rec.get("traffic_bytes_per_launch")
 
 
+def _time_ms(fn, reps, warmup=3):
+    """Mean duration of fn() over reps calls, by HIP events on torch's current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def cascade_report(dev, seed):
+    """Cascade attention (attn_cascade_fwd) against the plain call on batches whose requests
+    share a prefix: decode batches with long shared prefixes, and layer pass 0 of the mixed
+    long-context workload. One JSON line per batch: both times, the speedup, the K/V bytes a
+    per-request read would touch ('logical') and the largest output difference."""
+    import torch
+    import exact_softmax_attention_paged_amd as A
+    import gen
+    rng = np.random.default_rng(seed)
+    cases = []
+    for nd, pre, lo, hi in ((120, 2048, 4096, 32768), (256, 4096, 4224, 6144),
+                            (256, 8192, 8448, 12288), (64, 16384, 16896, 20480)):
+        sl = rng.integers(lo, hi, size=nd, endpoint=True)
+        b = gen.make_batch(f"{nd} decodes, ctx U[{lo},{hi}], {pre}-token shared prefix",
+                           num_heads=64, num_kv_heads=8, head_size=128, block_size=64,
+                           dtype="bf16", query_lens=[1] * nd, seq_lens=sl, passes=[(True, 0)],
+                           seed=seed, shared_prefix_blocks=pre // 64)
+        cases.append(b)
+    cases.append(gen.config(5, seed=seed))
+    for b in cases:
+        q, kv = gen.make_tensors(b, seed, dev)
+        bt, qsl, sl = (torch.from_numpy(x).to(dev) for x in (b.block_table, b.query_start_loc,
+                                                             b.seq_lens))
+        P = b.shared_prefix_blocks * b.block_size
+        desc = A.make_desc(num_seqs=b.num_seqs, num_tokens=b.num_tokens,
+                           num_decodes=b.num_decodes, max_query_len=b.max_query_len,
+                           max_seq_len=b.max_seq_len, num_heads=b.num_heads,
+                           num_kv_heads=b.num_kv_heads, head_size=b.head_size,
+                           num_blocks=b.num_blocks, block_size=b.block_size,
+                           max_blocks_per_seq=b.max_blocks_per_seq, dtype=A.ATTN_BF16)
+        out = torch.empty_like(q)
+        lse = torch.empty(b.num_tokens, b.num_heads, dtype=torch.float32, device=dev)
+        wsp = torch.empty(max(A.attn_workspace_bytes(desc), 1), dtype=torch.uint8, device=dev)
+        wsc = torch.empty(A.attn_cascade_workspace_bytes(desc, P), dtype=torch.uint8, device=dev)
+        causal = b.passes[0][0]
+        reps = 5 if b.num_tokens > 1000 else 20
+        tp = _time_ms(lambda: A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl, b.scale, causal, 0,
+                                                out, lse, wsp), reps)
+        ref = out.clone()
+        tc = _time_ms(lambda: A.attn_cascade_fwd(desc, q, kv, bt, qsl, sl, P, b.scale, causal,
+                                                 out, lse, wsc), reps)
+        diff = (out.float() - ref.float()).abs().max().item()
+        logical = int(b.seq_lens[:b.num_decodes].astype(np.int64).sum()) * 2 * b.num_kv_heads * \
+            b.head_size * 2
+        print(json.dumps({"report": "cascade", "batch": b.name, "common_prefix_len": P,
+                          "plain_ms": round(tp, 4), "cascade_ms": round(tc, 4),
+                          "speedup": round(tp / tc, 3), "decode_kv_gb_logical": logical / 1e9,
+                          "max_abs_diff_vs_plain": diff}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +271,9 @@ def main():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/prefill_traffic.json from two rocprofv3 --pmc runs")
     ap.add_argument("--record-command", default="", help="command line stored with the record")
+    ap.add_argument("--report", choices=["cascade"],
+                    help="instead of the headline step, time one of the next-step paths "
+                         "against the plain path and print one JSON line per batch")
     args = ap.parse_args()
     if args.record_traffic:
         record_traffic(args.record_traffic[0], args.record_traffic[1], args.record_command)
@@ -226,6 +294,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.pmc_probe:
         pmc_probe(dev)
+    if args.report == "cascade":
+        cascade_report(dev, args.seed)
+        return
     batch = gen.config(5, seed=args.seed)
     nd = batch.num_decodes
     tok0 = int(batch.query_start_loc[nd])

@@ -65,12 +65,32 @@ size_t workspace_for(const attn_desc* d, int64_t max_parts) {
 
 size_t round256(int64_t bytes) { return (size_t)ceil_div(bytes, 256) * 256; }
 
+// Key slices of the cascade prefix pass. Its rows are the (token, q head) pairs of each GQA
+// group, 256 per workgroup; with few rows the prefix keys are split into slices (at least 512
+// keys each, a multiple of the 64-key tile) until about 512 workgroups run.
+struct PrefixSplit {
+  int32_t slices, slice_keys;
+};
+PrefixSplit prefix_split(const attn_desc* d, int32_t prefix) {
+  const int64_t rows = (int64_t)d->num_tokens * (d->num_heads / d->num_kv_heads);
+  const int64_t wgs = ceil_div(rows, 256) * d->num_kv_heads;
+  int64_t s = ceil_div(512, wgs);
+  const int64_t max_s = ceil_div(prefix, 512);
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  const int64_t keys = ceil_div(ceil_div(prefix, s), 64) * 64;
+  return {(int32_t)ceil_div(prefix, keys), (int32_t)keys};
+}
+
 // Cascade workspace: the prefix pass's fp32 partial result for every query row
-// ([num_tokens][Hq][d], then [num_tokens][Hq] log-sum-exps), followed by the decode
-// partitions' workspace of the suffix pass.
-size_t cascade_prefix_bytes(const attn_desc* d) {
+// ([num_tokens][Hq][d], then [num_tokens][Hq] log-sum-exps); with key slices, the slices'
+// partial results in the same layout, slice after slice; then the decode partitions'
+// workspace of the suffix pass.
+size_t cascade_prefix_bytes(const attn_desc* d, int32_t prefix) {
   const int64_t rows = (int64_t)d->num_tokens * d->num_heads;
-  return round256(rows * d->head_size * 4) + round256(rows * 4);
+  const PrefixSplit sp = prefix_split(d, prefix);
+  const int64_t copies = sp.slices > 1 ? 1 + sp.slices : 1;
+  return copies * (round256(rows * d->head_size * 4) + round256(rows * 4));
 }
 
 attn::PrefillParams prefill_params(const attn_desc& d, const void* q, const void* kv_cache,
@@ -135,6 +155,7 @@ attn_status check_cascade(const attn_desc* d, int32_t common_prefix_len) {
   if (common_prefix_len < 0 || common_prefix_len % d->block_size != 0 ||
       common_prefix_len > d->max_seq_len)
     return ATTN_ERR_SHAPE;
+  if ((int64_t)d->num_tokens * d->num_heads >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
 
@@ -197,7 +218,7 @@ attn_status attn_cascade_workspace_bytes(const attn_desc* desc, int32_t common_p
   const attn_status s = check_cascade(desc, common_prefix_len);
   if (s != ATTN_OK) return s;
   const size_t suffix = workspace_for(desc, decode_max_parts(desc, 0));
-  *bytes = common_prefix_len == 0 ? suffix : cascade_prefix_bytes(desc) + suffix;
+  *bytes = common_prefix_len == 0 ? suffix : cascade_prefix_bytes(desc, common_prefix_len) + suffix;
   return ATTN_OK;
 }
 
@@ -218,25 +239,46 @@ attn_status attn_cascade_fwd(const attn_desc* desc, const void* q, const void* k
       query_start_loc == nullptr || seq_lens == nullptr || out == nullptr)
     return ATTN_ERR_NULL;
   const int64_t max_parts = decode_max_parts(&d, 0);
-  const size_t pre_bytes = cascade_prefix_bytes(&d);
+  const size_t pre_bytes = cascade_prefix_bytes(&d, common_prefix_len);
   const size_t need = pre_bytes + workspace_for(&d, max_parts);
   if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  float* pre_o = static_cast<float*>(workspace);
-  float* pre_lse = pre_o + round256((int64_t)d.num_tokens * d.num_heads * d.head_size * 4) / 4;
-  float* ws_suffix = reinterpret_cast<float*>(static_cast<char*>(workspace) + pre_bytes);
+  const int64_t rows = (int64_t)d.num_tokens * d.num_heads;
+  const size_t copy_bytes = round256(rows * d.head_size * 4) + round256(rows * 4);
+  char* const wsb = static_cast<char*>(workspace);
+  float* pre_o = reinterpret_cast<float*>(wsb);
+  float* pre_lse = reinterpret_cast<float*>(wsb + round256(rows * d.head_size * 4));
+  float* ws_suffix = reinterpret_cast<float*>(wsb + pre_bytes);
   const int32_t skip = common_prefix_len / d.block_size;
+  const PrefixSplit sp = prefix_split(&d, common_prefix_len);
 
-  // 1. prefix pass: every query token of the batch against the shared prefix, no mask
+  // 1. prefix pass: every query token of the batch against the shared prefix, no mask;
+  //    with key slices, each slice's partial result goes to its own copy, merged afterwards
   attn::PrefillParams pre = prefill_params(d, q, kv_cache, block_table, query_start_loc,
                                            seq_lens, scale, 0, 0, nullptr, pre_lse);
   pre.single_ql = d.num_tokens;
   pre.single_sl = common_prefix_len;
-  pre.max_query_len = d.num_tokens;
   pre.num_seqs = 1;
   pre.out_f32 = pre_o;
+  if (sp.slices > 1) {
+    pre.single_slice = sp.slice_keys;
+    pre.slice_stride = rows;
+    pre.out_f32 = reinterpret_cast<float*>(wsb + copy_bytes);
+    pre.lse = reinterpret_cast<float*>(wsb + copy_bytes + (size_t)sp.slices *
+                                       round256(rows * d.head_size * 4));
+  }
   if (attn::launch_prefill_bf16(pre, st) != hipSuccess) return ATTN_ERR_HIP;
+  if (sp.slices > 1) {
+    attn::PrefixMergeParams mp{};
+    mp.o_in = pre.out_f32;
+    mp.lse_in = pre.lse;
+    mp.o_out = pre_o;
+    mp.lse_out = pre_lse;
+    mp.rows = rows;
+    mp.slices = sp.slices;
+    if (attn::launch_prefix_slices_merge(mp, d.head_size, st) != hipSuccess) return ATTN_ERR_HIP;
+  }
 
   // 2. suffix pass over the keys after the prefix, merged with the prefix result
   attn::PrefillParams pp = prefill_params(d, q, kv_cache, block_table, query_start_loc,

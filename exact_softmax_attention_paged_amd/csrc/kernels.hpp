@@ -30,7 +30,13 @@ struct PrefillParams {
                                 // shared prefix); seq_len shrinks by kv_skip_blocks*block_size
   int32_t single_ql, single_sl; // single_ql > 0: one sequence whose queries are rows
                                 // [0, single_ql) of q and whose keys are the first single_sl
-                                // keys of block-table row 0 (the prefix pass)
+                                // keys of block-table row 0 (the prefix pass, no mask). Its
+                                // rows are (token, q head) pairs of one kv head's GQA group
+                                // (grid y = kv head), and grid z splits the keys into slices
+                                // of single_slice keys (a multiple of 64), slice z writing its
+                                // partial result at out_f32 / lse + z * slice_stride rows
+  int32_t single_slice;
+  int64_t slice_stride;         // (token, head) rows between slices of out_f32 and lse
   float* out_f32;               // non-null: write O (normalised) in fp32 here, not to out
   const float* init_o;          // non-null: start each row from a partial result over
   const float* init_lse;        // earlier keys, fp32 [token][head][d] and [token][head]
@@ -71,7 +77,20 @@ __host__ __device__ inline void decode_partitions(int32_t seq_len, int32_t windo
   *count = end > f ? end - f : 0;
 }
 
+// Merge of the key slices of the cascade prefix pass: rows = num_tokens * num_heads;
+// slice z of row i is o_in[(z * rows + i) * d ..] and lse_in[z * rows + i].
+struct PrefixMergeParams {
+  const float* o_in;
+  const float* lse_in;
+  float* o_out;                 // [rows][d]
+  float* lse_out;               // [rows]
+  int64_t rows;
+  int32_t slices;
+};
+
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_prefix_slices_merge(const PrefixMergeParams& p, int head_size,
+                                      hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
 

@@ -103,16 +103,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   __shared__ __attribute__((aligned(1024))) unsigned char sKV[kBufs * 2 * TILEB];
 
   const bool single = p.single_ql > 0;          // cascade prefix pass: one sequence
+  const int group = p.num_heads / p.num_kv_heads;
   const int r = single ? 0 : p.seq_begin + blockIdx.z;
-  const int hq = blockIdx.y;
   const int qt = gridDim.x - 1 - blockIdx.x;   // longest (causal) tiles are dispatched first
   const int q_start = single ? 0 : p.qsl[r];
-  const int ql = single ? p.single_ql : p.qsl[r + 1] - q_start;
+  // query rows of this workgroup's sequence: its tokens, or in the prefix pass the
+  // (token, q head) pairs of one GQA group
+  const int ql = single ? p.single_ql * group : p.qsl[r + 1] - q_start;
   if (qt * kBR >= ql) return;
   // keys of this pass: [0, sl) after skipping kv_skip_blocks leading blocks
   const int sl = single ? p.single_sl : p.seq_lens[r] - p.kv_skip_blocks * p.block_size;
   const int cl = sl - ql;
-  const int kvh = hq / (p.num_heads / p.num_kv_heads);
+  const int kvh = single ? (int)blockIdx.y : (int)blockIdx.y / group;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave index, uniform
@@ -124,14 +126,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   const __bf16* __restrict__ kcache = static_cast<const __bf16*>(p.kv);
   const __bf16* __restrict__ vcache = kcache + p.v_offset;
   const int32_t* __restrict__ bt = p.block_table + (int64_t)r * p.max_blocks + p.kv_skip_blocks;
-  const int64_t row_stride = (int64_t)p.num_heads * D;   // q/out stride between tokens
+
+  // (token, q head) row of this lane's query column, as an index into [token][head] arrays
+  const int wrow0 = qt * kBR + w * kRows;                // first query row of this wave
+  const int my_row = min(wrow0 + lq, ql - 1);            // rows past ql: any valid row
+  const int64_t my_th = single
+      ? (int64_t)(my_row / group) * p.num_heads + kvh * group + my_row % group
+      : (int64_t)(q_start + my_row) * p.num_heads + blockIdx.y;
 
   // ---- Q^T (B operand): lane l holds query lq, d = 16c + 8h .. +7
-  const int wrow0 = qt * kBR + w * kRows;                // first query row of this wave
   bf16x8 qf[KC];
   {
-    const int row = min(wrow0 + lq, ql - 1);             // rows past ql: any valid row
-    const __bf16* src = q + (int64_t)(q_start + row) * row_stride + (int64_t)hq * D + 8 * h;
+    const __bf16* src = q + my_th * D + 8 * h;
 #pragma unroll
     for (int c = 0; c < KC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(src + 16 * c);
   }
@@ -141,8 +147,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   const int row_hi = min(ql, row_lo + kBR) - 1;
   const int kv_hi = CAUSAL ? min(sl, cl + row_hi + 1) : sl;
   const int kv_lo = WINDOW ? max(0, cl + row_lo - p.window + 1) : 0;
-  const int t_begin = kv_lo / kBC;
-  const int t_end = (kv_hi + kBC - 1) / kBC;
+  int t_begin = kv_lo / kBC;
+  int t_end = (kv_hi + kBC - 1) / kBC;
+  if (single && p.single_slice > 0) {           // this workgroup's slice of the keys
+    t_begin = (int)blockIdx.z * (p.single_slice / kBC);
+    t_end = min(t_end, t_begin + p.single_slice / kBC);
+  }
   const int w_row_lo = wrow0;
   const int w_row_hi = min(ql, wrow0 + kRows) - 1;
   const bool wave_active = w_row_lo <= w_row_hi;
@@ -248,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   // O = o0, l = 1 with the reference max m = lse0 / scale: the prefix's sum of
   // exp(scale (s - m)) is exp(lse0 - scale m) = 1.
   if (p.init_o != nullptr) {
-    const int64_t ri = (int64_t)(q_start + min(wrow0 + lq, ql - 1)) * p.num_heads + hq;
+    const int64_t ri = my_th;
     const float lse0 = p.init_lse[ri];
     if (lse0 > -INFINITY) {
       m_ref = lse0 / p.scale;
@@ -398,7 +408,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   const int row = wrow0 + lq;
   if (row < ql) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int64_t off = (int64_t)(q_start + row) * row_stride + (int64_t)hq * D + 4 * h;
+    const int64_t th = my_th + (single ? (int64_t)blockIdx.z * p.slice_stride : 0);
+    const int64_t off = th * D + 4 * h;
     if (p.out_f32 != nullptr) {
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc)
@@ -422,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
         }
     }
     if (p.lse != nullptr && h == 0) {
-      p.lse[(int64_t)(q_start + row) * p.num_heads + hq] =
+      p.lse[th] =
           l_tot > 0.f ? p.scale * m_ref + __logf(l_tot) : -INFINITY;
     }
   }
@@ -430,7 +441,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
 
 template <int D, bool CAUSAL, bool WINDOW>
 hipError_t launch(const PrefillParams& p, hipStream_t stream) {
-  const dim3 grid((p.max_query_len + kBR - 1) / kBR, p.num_heads, p.num_seqs);
+  dim3 grid((p.max_query_len + kBR - 1) / kBR, p.num_heads, p.num_seqs);
+  if (p.single_ql > 0) {            // prefix pass: (token, head) rows per kv head, key slices
+    const int rows = p.single_ql * (p.num_heads / p.num_kv_heads);
+    const int slices = p.single_slice > 0 ? (p.single_sl + p.single_slice - 1) / p.single_slice : 1;
+    grid = dim3((rows + kBR - 1) / kBR, p.num_kv_heads, slices);
+  }
   hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, WINDOW>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

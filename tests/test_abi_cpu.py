@@ -189,6 +189,11 @@ def test_cascade_workspace_size():
     pre = -(-(rows * 128 * 4) // 256) * 256 + -(-(rows * 4) // 256) * 256
     assert A.attn_cascade_workspace_bytes(d, 16) == pre + plain
     assert A.attn_cascade_workspace_bytes(_desc(num_decodes=0), 32) == pre
+    # few rows and a long prefix: the prefix keys are split into slices of >= 512 keys, each
+    # with its own copy of the partial result (here 4 slices of 512 keys, plus the merged copy)
+    big = _desc(num_decodes=0, max_seq_len=4096, max_blocks_per_seq=256)
+    assert A.attn_cascade_workspace_bytes(big, 2048) == 5 * pre
+    assert A.attn_cascade_workspace_bytes(big, 512) == pre
 
 
 def test_cascade_checker():

@@ -56,6 +56,10 @@ CASES = [
                                          hq=8, hkv=2, d=128, bs=64, prefix_blocks=4), 128),
     ("mixed-d64-gqa20-bs64", dict(ql=[1, 1, 600, 129], cl=[1100, 1024, 1024, 3000], hq=40,
                                   hkv=2, d=64, bs=64, prefix_blocks=16), 0),
+    # few query rows and a long prefix: the prefix pass splits its keys into 8 slices
+    ("decode-d128-gqa8-bs64-8slices", dict(ql=[1] * 6 + [50],
+                                           cl=[4096, 4200, 5000, 4097, 6000, 4500, 4096],
+                                           hq=16, hkv=2, d=128, bs=64, prefix_blocks=64), 0),
 ]
 
 
