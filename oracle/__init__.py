@@ -7,6 +7,7 @@ Python binding never do. It shares no code with the HIP path.
 from .naive_attention import (attention, attend_rows, gather_kv, visible_keys,
                               softmax_weights, flops_visible_pairs)
 from .cascade import cascade_attention, merge_partials
+from .kv_write import kv_cache_write
 
 __all__ = ["attention", "attend_rows", "gather_kv", "visible_keys", "softmax_weights",
-           "flops_visible_pairs", "cascade_attention", "merge_partials"]
+           "flops_visible_pairs", "cascade_attention", "merge_partials", "kv_cache_write"]
