@@ -259,6 +259,35 @@ def cascade_report(dev, seed):
                           "max_abs_diff_vs_plain": diff}), flush=True)
 
 
+def kv_write_report(dev, seed):
+    """KV-cache write (attn_kv_cache_write) throughput. Algorithmic bytes per token: its K and
+    V rows read once and written once (4 * num_kv_heads * head_size * 2 bytes in bf16) plus
+    its 8-byte slot. One JSON line per shape, against the 8 TB/s HBM roofline."""
+    import torch
+    import exact_softmax_attention_paged_amd as A
+    import gen
+    b = gen.config(5, seed=seed)
+    hkv, d, bs, nb = b.num_kv_heads, b.head_size, b.block_size, b.num_blocks
+    cache = torch.zeros((2, nb, bs, hkv, d), dtype=torch.bfloat16, device=dev)
+    rng = np.random.default_rng(seed)
+    for T, what in ((b.num_tokens, "the mixed workload's 16504 new tokens"),
+                    (262144, "262144 new tokens")):
+        slots = torch.from_numpy(rng.permutation(nb * bs)[:T].astype(np.int64)).to(dev)
+        key = torch.randn(T, hkv, d, device=dev).to(torch.bfloat16)
+        val = torch.randn(T, hkv, d, device=dev).to(torch.bfloat16)
+        desc = A.make_desc(num_seqs=1, num_tokens=T, num_decodes=0, max_query_len=1,
+                           max_seq_len=bs, num_heads=hkv, num_kv_heads=hkv, head_size=d,
+                           num_blocks=nb, block_size=bs, max_blocks_per_seq=1,
+                           dtype=A.ATTN_BF16)
+        ms = _time_ms(lambda: A.attn_kv_cache_write(desc, key, val, slots, cache), 50)
+        byts = T * (4 * hkv * d * 2 + 8)
+        print(json.dumps({"report": "kv-write", "shape": f"{what}, {hkv} kv heads, d {d}, "
+                          f"bf16, block 64, {nb} blocks", "tokens": T, "ms": round(ms, 5),
+                          "bytes": byts, "gbps": round(byts / (ms / 1e3) / 1e9, 1),
+                          "frac_of_8tbps": round(byts / (ms / 1e3) / PEAK_HBM_BYTES, 4)}),
+              flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,7 +300,7 @@ def main():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/prefill_traffic.json from two rocprofv3 --pmc runs")
     ap.add_argument("--record-command", default="", help="command line stored with the record")
-    ap.add_argument("--report", choices=["cascade"],
+    ap.add_argument("--report", choices=["cascade", "kv-write"],
                     help="instead of the headline step, time one of the next-step paths "
                          "against the plain path and print one JSON line per batch")
     args = ap.parse_args()
@@ -296,6 +325,9 @@ def main():
         pmc_probe(dev)
     if args.report == "cascade":
         cascade_report(dev, args.seed)
+        return
+    if args.report == "kv-write":
+        kv_write_report(dev, args.seed)
         return
     batch = gen.config(5, seed=args.seed)
     nd = batch.num_decodes

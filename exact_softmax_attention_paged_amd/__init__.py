@@ -23,7 +23,7 @@ ATTN_BF16, ATTN_F32 = 0, 1
 
 EXPORTED = ("attn_workspace_bytes", "attn_varlen_fwd", "attn_check_metadata_host",
             "attn_cascade_workspace_bytes", "attn_cascade_fwd", "attn_check_cascade_host",
-            "attn_status_str")
+            "attn_kv_cache_write", "attn_check_slot_mapping_host", "attn_status_str")
 
 
 class attn_desc(ctypes.Structure):
@@ -68,6 +68,11 @@ def lib():
         L.attn_cascade_fwd.restype = i32
         L.attn_check_cascade_host.argtypes = [P(attn_desc), vp, vp, vp, i32]
         L.attn_check_cascade_host.restype = i32
+        i64 = ctypes.c_int64
+        L.attn_kv_cache_write.argtypes = [P(attn_desc), vp, i64, vp, i64, vp, vp, vp]
+        L.attn_kv_cache_write.restype = i32
+        L.attn_check_slot_mapping_host.argtypes = [P(attn_desc), vp]
+        L.attn_check_slot_mapping_host.restype = i32
         L.attn_status_str.argtypes = [i32]
         L.attn_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -231,3 +236,47 @@ def varlen_fwd(q, kv_cache, block_table, query_start_loc, seq_lens, *, scale, ca
     attn_varlen_fwd(desc, q, kv_cache, block_table, query_start_loc, seq_lens, scale, causal,
                     window, out, lse, workspace)
     return out, lse
+
+
+def attn_check_slot_mapping_host(desc: attn_desc, slot_mapping: np.ndarray) -> int:
+    """Returns the status code of the host-side slot_mapping check."""
+    a = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    return int(lib().attn_check_slot_mapping_host(ctypes.byref(desc),
+                                                  a.ctypes.data_as(ctypes.c_void_p)))
+
+
+def attn_kv_cache_write(desc: attn_desc, key, value, slot_mapping, kv_cache,
+                        stream=None) -> None:
+    """Queue the write of the new tokens' K/V rows into kv_cache at slot_mapping.
+
+    key / value: [num_tokens, num_kv_heads, head_size] views whose last two dimensions are
+    contiguous (the token stride may be larger, e.g. columns of a packed QKV tensor);
+    slot_mapping: int64 [num_tokens]; kv_cache: [2, num_blocks, block_size, num_kv_heads,
+    head_size]; all on one GPU, dtype of desc."""
+    import torch
+    dev = kv_cache.device
+    if dev.type != "cuda":
+        raise ValueError("attn_kv_cache_write runs on a GPU device; kv_cache is on " + str(dev))
+    dt = torch.bfloat16 if desc.dtype == ATTN_BF16 else torch.float32
+    row = desc.num_kv_heads * desc.head_size
+    for name, t in (("key", key), ("value", value)):
+        if t.dtype != dt or t.device != dev:
+            raise TypeError(f"{name} must be {dt} on {dev}")
+        if tuple(t.shape) != (desc.num_tokens, desc.num_kv_heads, desc.head_size) or \
+                t.stride(2) != 1 or t.stride(1) != desc.head_size or t.stride(0) < row:
+            raise ValueError(f"{name} must be [num_tokens, num_kv_heads, head_size] with "
+                             "contiguous heads")
+    _check_tensor("slot_mapping", slot_mapping, torch.int64, dev)
+    _check_tensor("kv_cache", kv_cache, dt, dev)
+    if slot_mapping.numel() != desc.num_tokens:
+        raise ValueError("slot_mapping must hold num_tokens entries")
+    if tuple(kv_cache.shape) != (2, desc.num_blocks, desc.block_size, desc.num_kv_heads,
+                                 desc.head_size):
+        raise ValueError("kv_cache shape does not match desc")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = lib().attn_kv_cache_write(ctypes.byref(desc), _ptr(key), int(key.stride(0)),
+                                   _ptr(value), int(value.stride(0)), _ptr(slot_mapping),
+                                   _ptr(kv_cache), ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_kv_cache_write")

@@ -4,7 +4,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
+#include <vector>
 
 #include "kernels.hpp"
 
@@ -342,6 +344,65 @@ attn_status attn_check_metadata_host(const attn_desc* desc, const int32_t* block
       if (blk < 0 || blk >= d.num_blocks) return ATTN_ERR_METADATA;
     }
   }
+  return ATTN_OK;
+}
+
+attn_status attn_kv_cache_write(const attn_desc* desc, const void* key, int64_t key_row_stride,
+                                const void* value, int64_t value_row_stride,
+                                const int64_t* slot_mapping, void* kv_cache, void* stream) {
+  if (desc == nullptr) return ATTN_ERR_NULL;
+  const attn_desc& d = *desc;
+  if (d.num_tokens < 0 || d.num_kv_heads <= 0 || d.num_blocks < 0) return ATTN_ERR_SHAPE;
+  if (d.block_size <= 0 || d.block_size % 16 != 0) return ATTN_ERR_BLOCK_SIZE;
+  if (d.head_size != 64 && d.head_size != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d.dtype != ATTN_BF16 && d.dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  const int64_t elem = d.dtype == ATTN_BF16 ? 2 : 4;
+  const int64_t row = (int64_t)d.num_kv_heads * d.head_size;        // elements per token row
+  if (key_row_stride < row || value_row_stride < row) return ATTN_ERR_SHAPE;
+  // 16-byte chunks: rows must start on 16-byte boundaries
+  if ((key_row_stride * elem) % 16 != 0 || (value_row_stride * elem) % 16 != 0)
+    return ATTN_ERR_SHAPE;
+  if ((int64_t)d.num_tokens * 2 * (row * elem / 16) / 256 >= ((int64_t)1 << 31))
+    return ATTN_ERR_SHAPE;                                          // grid x limit
+  if (d.num_tokens == 0) return ATTN_OK;
+  if (key == nullptr || value == nullptr || slot_mapping == nullptr || kv_cache == nullptr)
+    return ATTN_ERR_NULL;
+  if ((uintptr_t)key % 16 != 0 || (uintptr_t)value % 16 != 0 || (uintptr_t)kv_cache % 16 != 0)
+    return ATTN_ERR_SHAPE;
+  attn::KvWriteParams p{};
+  p.key = key;
+  p.value = value;
+  p.slot_mapping = slot_mapping;
+  p.kv_cache = kv_cache;
+  p.num_tokens = d.num_tokens;
+  p.key_stride_bytes = key_row_stride * elem;
+  p.value_stride_bytes = value_row_stride * elem;
+  p.slot_bytes = row * elem;
+  p.row_chunks = p.slot_bytes / 16;
+  p.num_slots = (int64_t)d.num_blocks * d.block_size;
+  p.v_offset_bytes = p.num_slots * p.slot_bytes;
+  return attn::launch_kv_write(p, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK
+                                                                                : ATTN_ERR_HIP;
+}
+
+attn_status attn_check_slot_mapping_host(const attn_desc* desc, const int64_t* slot_mapping) {
+  if (desc == nullptr) return ATTN_ERR_NULL;
+  const attn_desc& d = *desc;
+  if (d.num_tokens < 0 || d.num_blocks < 0) return ATTN_ERR_SHAPE;
+  if (d.block_size <= 0 || d.block_size % 16 != 0) return ATTN_ERR_BLOCK_SIZE;
+  if (d.num_tokens == 0) return ATTN_OK;
+  if (slot_mapping == nullptr) return ATTN_ERR_NULL;
+  const int64_t num_slots = (int64_t)d.num_blocks * d.block_size;
+  std::vector<int64_t> seen;
+  seen.reserve((size_t)d.num_tokens);
+  for (int32_t t = 0; t < d.num_tokens; ++t) {
+    const int64_t s = slot_mapping[t];
+    if (s >= num_slots) return ATTN_ERR_METADATA;
+    if (s >= 0) seen.push_back(s);
+  }
+  std::sort(seen.begin(), seen.end());
+  for (size_t i = 1; i < seen.size(); ++i)
+    if (seen[i] == seen[i - 1]) return ATTN_ERR_METADATA;
   return ATTN_OK;
 }
 

@@ -88,7 +88,23 @@ struct PrefixMergeParams {
   int32_t slices;
 };
 
+// KV-cache write: token t's K row (key + t * key_stride_bytes) and V row go to slot
+// slot_mapping[t] of the K and V halves of the cache.
+struct KvWriteParams {
+  const void* key;
+  const void* value;
+  const int64_t* slot_mapping;
+  void* kv_cache;
+  int64_t num_tokens;
+  int64_t key_stride_bytes, value_stride_bytes;
+  int64_t row_chunks;           // 16-byte chunks of one token's row (num_kv_heads * head_size)
+  int64_t slot_bytes;           // bytes of one slot = one token's row
+  int64_t num_slots;            // num_blocks * block_size
+  int64_t v_offset_bytes;       // bytes from the K half to the V half
+};
+
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t stream);
 hipError_t launch_prefix_slices_merge(const PrefixMergeParams& p, int head_size,
                                       hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);

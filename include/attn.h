@@ -200,6 +200,46 @@ attn_status attn_check_cascade_host(const attn_desc* desc, const int32_t* block_
                                     const int32_t* query_start_loc, const int32_t* seq_lens,
                                     int32_t common_prefix_len);
 
+/*
+ * attn_kv_cache_write: store the new tokens' K and V rows in the paged cache through
+ * slot_mapping ([FA] FlashAttentionMetadata section: slot_mapping beside block_table;
+ * "왜 이 설계인가" item 2: block_table and slot_mapping reach a non-contiguous cache; cache
+ * shape from the FlashAttentionBackend section). This is the step before attention in a layer:
+ * afterwards attn_varlen_fwd reads these tokens through block_table.
+ *
+ * For t in [0, desc->num_tokens) with s = slot_mapping[t] >= 0:
+ *   kv_cache[0][s / block_size][s % block_size][h][x] = key  [t * key_row_stride + h * head_size + x]
+ *   kv_cache[1][s / block_size][s % block_size][h][x] = value[t * value_row_stride + h * head_size + x]
+ * for every kv head h and x < head_size. A negative slot marks a padding token and writes
+ * nothing; a slot >= num_blocks * block_size is skipped as well (never written out of bounds).
+ * Slots of one call must be distinct (attn_check_slot_mapping_host checks host copies).
+ *
+ * Arguments (device pointers unless noted):
+ *   desc             host pointer; uses num_tokens (new tokens), num_kv_heads, head_size,
+ *                    num_blocks, block_size and dtype (of key, value and kv_cache alike).
+ *   key, value       token rows of num_kv_heads * head_size elements, key_row_stride /
+ *                    value_row_stride elements apart (>= num_kv_heads * head_size; e.g. the K
+ *                    and V columns of a packed QKV projection). Rows must start on 16-byte
+ *                    boundaries.
+ *   slot_mapping     int64 [num_tokens].
+ *   kv_cache         [2][num_blocks][block_size][num_kv_heads][head_size], updated in place.
+ *   stream           hipStream_t (NULL = the null stream); the call returns once queued.
+ * Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE (negative sizes, row strides smaller than a row or
+ * not 16-byte multiples, misaligned pointers, more than 2^39 chunks), ATTN_ERR_BLOCK_SIZE,
+ * ATTN_ERR_UNSUPPORTED (head_size not 64/128, unknown dtype), ATTN_ERR_HIP.
+ */
+attn_status attn_kv_cache_write(const attn_desc* desc, const void* key, int64_t key_row_stride,
+                                const void* value, int64_t value_row_stride,
+                                const int64_t* slot_mapping, void* kv_cache, void* stream);
+
+/*
+ * attn_check_slot_mapping_host: every slot of the host array slot_mapping[num_tokens] is
+ * negative (padding) or below num_blocks * block_size, and the non-negative slots are
+ * distinct. Returns ATTN_OK, ATTN_ERR_METADATA, ATTN_ERR_NULL, ATTN_ERR_SHAPE or
+ * ATTN_ERR_BLOCK_SIZE.
+ */
+attn_status attn_check_slot_mapping_host(const attn_desc* desc, const int64_t* slot_mapping);
+
 /* attn_status_str: static, NUL-terminated name of a status code ("ATTN_OK", ...). */
 const char* attn_status_str(int32_t status);
 

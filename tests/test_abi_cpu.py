@@ -216,3 +216,43 @@ def test_cascade_binding_refuses_cpu_tensors():
     q = torch.zeros(5, 8, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         A.attn_cascade_fwd(_desc(), q, q, q, q, q, 16, 0.1, True, q, None, None)
+
+
+# ---------------------------------------------------------------- KV-cache write
+def _kvw(desc, ks=256, vs=256, key=FAKE, value=FAKE, slots=FAKE, cache=FAKE):
+    return A.lib().attn_kv_cache_write(ctypes.byref(desc) if desc is not None else None, key,
+                                       ks, value, vs, slots, cache, None)
+
+
+def test_kv_write_argument_errors():
+    d = _desc()                                       # Hkv 2, d 128: rows of 256 elements
+    assert _kvw(None) == A.ATTN_ERR_NULL
+    assert _kvw(d, key=None) == A.ATTN_ERR_NULL
+    assert _kvw(d, slots=None) == A.ATTN_ERR_NULL
+    assert _kvw(d, ks=255) == A.ATTN_ERR_SHAPE        # smaller than a row
+    assert _kvw(d, vs=260) == A.ATTN_ERR_SHAPE        # 520 bytes: not a 16-byte multiple
+    assert _kvw(d, key=ctypes.c_void_p(0x1008)) == A.ATTN_ERR_SHAPE   # misaligned
+    assert _kvw(_desc(block_size=24)) == A.ATTN_ERR_BLOCK_SIZE
+    assert _kvw(_desc(head_size=80)) == A.ATTN_ERR_UNSUPPORTED
+    assert _kvw(_desc(dtype=5)) == A.ATTN_ERR_UNSUPPORTED
+    assert _kvw(_desc(num_tokens=-1)) == A.ATTN_ERR_SHAPE
+    assert _kvw(_desc(num_tokens=0), key=None, value=None, slots=None, cache=None) == A.ATTN_OK
+
+
+def test_slot_mapping_checker():
+    d = _desc(num_tokens=4)                           # 8 blocks x 16 slots
+    ok = np.array([5, -1, 127, 16], np.int64)
+    assert A.attn_check_slot_mapping_host(d, ok) == A.ATTN_OK
+    assert A.attn_check_slot_mapping_host(d, np.array([5, -1, 128, 16], np.int64)) == \
+        A.ATTN_ERR_METADATA                           # past the cache
+    assert A.attn_check_slot_mapping_host(d, np.array([5, 9, 5, -1], np.int64)) == \
+        A.ATTN_ERR_METADATA                           # duplicate
+    assert A.attn_check_slot_mapping_host(d, np.array([-1, -1, -3, -1], np.int64)) == A.ATTN_OK
+
+
+def test_kv_write_binding_refuses_cpu_tensors():
+    import torch
+    k = torch.zeros(5, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        A.attn_kv_cache_write(_desc(), k, k, torch.zeros(5, dtype=torch.int64),
+                              torch.zeros(2, 8, 16, 2, 128, dtype=torch.bfloat16))
