@@ -14,7 +14,9 @@ format or the scaling, so this module states its readings (also in the design no
   * one scale per tensor for K and one for V (fp32, > 0): a stored code c stands for
     value(c) * k_scale (or v_scale);
   * storing x: the code nearest to x / scale, ties to the even code (even mantissa), with
-    magnitudes beyond 448 saturated to 448 (NaN stays NaN);
+    magnitudes beyond 448 saturated to 448 (NaN stays a NaN code). The quotient x / scale is
+    formed in fp32 (IEEE, correctly rounded), the precision the storing kernel uses, so that
+    both sides take the rounding decision on the same value;
   * attention over the cache is the plain definition applied to the dequantised K and V.
 """
 from __future__ import annotations
@@ -43,9 +45,10 @@ _POS = np.array(sorted(set(float(x) for x in _ALL[:128] if np.isfinite(x))))   #
 
 
 def e4m3_quantize(x, scale: float) -> np.ndarray:
-    """uint8 codes of x / scale: nearest representable value, ties to the even mantissa,
-    magnitudes beyond 448 saturated, NaN to the NaN code 0x7F (sign kept)."""
-    y = np.asarray(x, dtype=np.float64) / float(scale)
+    """uint8 codes of x / scale (quotient in fp32): nearest representable value, ties to the
+    even mantissa, magnitudes beyond 448 saturated, NaN to a NaN code (0x7F with the sign)."""
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = (np.asarray(x, dtype=np.float32) / np.float32(scale)).astype(np.float64)
     mag = np.minimum(np.abs(np.nan_to_num(y, nan=0.0)), E4M3_MAX)
     i = np.searchsorted(_POS, mag)                 # _POS[i-1] < mag <= _POS[i]
     i = np.clip(i, 1, len(_POS) - 1)
