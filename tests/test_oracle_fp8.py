@@ -42,8 +42,8 @@ def test_quantizer_round_trip_ties_saturation_and_scale():
     # 1.1875 between 1.125 (1) and 1.25 (2) -> 1.25; same for negatives and subnormals
     t = of8.e4m3_quantize(np.array([1.0625, 1.1875, -1.0625, 1.5 * 2.0 ** -9, 2.5 * 2.0 ** -9]), 1.0)
     np.testing.assert_array_equal(of8.e4m3_value(t), [1.0, 1.25, -1.0, 2.0 ** -8, 2.0 ** -8])
-    # just off a tie goes to the nearer code
-    t = of8.e4m3_quantize(np.array([1.0625 + 1e-9, 1.1875 - 1e-9]), 1.0)
+    # just off a tie (by one fp32 step, the precision of the quotient) goes to the nearer code
+    t = of8.e4m3_quantize(np.array([1.0625 + 2.0 ** -23, 1.1875 - 2.0 ** -23]), 1.0)
     np.testing.assert_array_equal(of8.e4m3_value(t), [1.125, 1.125])
     s = of8.e4m3_quantize(np.array([464.0, 1e6, -1e30, 500.0]), 1.0)  # beyond 448 saturates
     np.testing.assert_array_equal(s, [0x7E, 0x7E, 0xFE, 0x7E])
