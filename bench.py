@@ -288,6 +288,55 @@ def kv_write_report(dev, seed):
               flush=True)
 
 
+def fp8_decode_report(dev, seed):
+    """Decode over an E4M3 cache (attn_fp8_decode_fwd) against the bf16 cache
+    (attn_varlen_fwd) on the paged GQA decode workload (256 requests, contexts U[512, 8192],
+    32 q / 8 kv heads, d 128, block 16) and on the mixed workload's 120 decode requests
+    (pass 0). Algorithmic bytes: each request's visible K and V once (2 bytes per element in
+    bf16, 1 in E4M3) plus q, out, lse and the block-table entries. One JSON line per
+    workload and cache type."""
+    import torch
+    import exact_softmax_attention_paged_amd as A
+    import gen
+    for k in (4, 5):
+        b = gen.config(k, seed=seed)
+        nd = b.num_decodes
+        if nd != b.num_seqs:          # the decode requests only
+            b = gen.subset_meta(b, list(range(nd)))
+        q = gen.make_q(b, seed, dev)
+        kv = gen.make_kv(b, seed, dev)
+        rng = np.random.default_rng(seed)
+        codes = torch.from_numpy(rng.integers(0, 256, size=tuple(kv.shape), dtype=np.uint8))
+        codes[(codes & 0x7F) == 0x7F] = 0
+        codes = codes.to(dev)
+        bt, qsl, sl = (torch.from_numpy(x).to(dev) for x in (b.block_table, b.query_start_loc,
+                                                             b.seq_lens))
+        desc = A.make_desc(num_seqs=b.num_seqs, num_tokens=b.num_tokens, num_decodes=nd,
+                           max_query_len=1, max_seq_len=b.max_seq_len, num_heads=b.num_heads,
+                           num_kv_heads=b.num_kv_heads, head_size=b.head_size,
+                           num_blocks=b.num_blocks, block_size=b.block_size,
+                           max_blocks_per_seq=b.max_blocks_per_seq, dtype=A.ATTN_BF16)
+        out = torch.empty_like(q)
+        lse = torch.empty(b.num_tokens, b.num_heads, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(A.attn_workspace_bytes(desc), 1), dtype=torch.uint8, device=dev)
+        keys = int(b.seq_lens.astype(np.int64).sum())
+        extra = nd * (b.num_heads * b.head_size * 2 * 2 + b.num_heads * 4) + \
+            int(sum(-(-int(x) // b.block_size) for x in b.seq_lens)) * 4
+        for name, elem, fn in (
+                ("bf16", 2, lambda: A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl, b.scale, True, 0,
+                                                      out, lse, ws)),
+                ("e4m3", 1, lambda: A.attn_fp8_decode_fwd(desc, q, codes, bt, qsl, sl, b.scale,
+                                                          0.0125, 0.02, 0, out, lse, ws))):
+            ms = _time_ms(fn, 20)
+            byts = keys * 2 * b.num_kv_heads * b.head_size * elem + extra
+            print(json.dumps({"report": "fp8-decode", "workload": gen.CONFIG_NAMES[k] +
+                              (" (its 120 decode requests)" if k == 5 else ""), "cache": name,
+                              "ms": round(ms, 4), "bytes": byts,
+                              "gbps": round(byts / (ms / 1e3) / 1e9, 1),
+                              "frac_of_8tbps": round(byts / (ms / 1e3) / PEAK_HBM_BYTES, 4),
+                              "tokens_per_s": round(keys / (ms / 1e3), 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -300,7 +349,7 @@ def main():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/prefill_traffic.json from two rocprofv3 --pmc runs")
     ap.add_argument("--record-command", default="", help="command line stored with the record")
-    ap.add_argument("--report", choices=["cascade", "kv-write"],
+    ap.add_argument("--report", choices=["cascade", "kv-write", "fp8-decode"],
                     help="instead of the headline step, time one of the next-step paths "
                          "against the plain path and print one JSON line per batch")
     args = ap.parse_args()
@@ -328,6 +377,9 @@ def main():
         return
     if args.report == "kv-write":
         kv_write_report(dev, args.seed)
+        return
+    if args.report == "fp8-decode":
+        fp8_decode_report(dev, args.seed)
         return
     batch = gen.config(5, seed=args.seed)
     nd = batch.num_decodes

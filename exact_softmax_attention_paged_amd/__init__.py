@@ -23,7 +23,8 @@ ATTN_BF16, ATTN_F32 = 0, 1
 
 EXPORTED = ("attn_workspace_bytes", "attn_varlen_fwd", "attn_check_metadata_host",
             "attn_cascade_workspace_bytes", "attn_cascade_fwd", "attn_check_cascade_host",
-            "attn_kv_cache_write", "attn_check_slot_mapping_host", "attn_status_str")
+            "attn_kv_cache_write", "attn_check_slot_mapping_host", "attn_kv_cache_write_fp8",
+            "attn_fp8_decode_fwd", "attn_status_str")
 
 
 class attn_desc(ctypes.Structure):
@@ -71,6 +72,12 @@ def lib():
         i64 = ctypes.c_int64
         L.attn_kv_cache_write.argtypes = [P(attn_desc), vp, i64, vp, i64, vp, vp, vp]
         L.attn_kv_cache_write.restype = i32
+        L.attn_kv_cache_write_fp8.argtypes = [P(attn_desc), vp, i64, vp, i64, vp, f32, f32, vp,
+                                              vp]
+        L.attn_kv_cache_write_fp8.restype = i32
+        L.attn_fp8_decode_fwd.argtypes = [P(attn_desc), vp, vp, vp, vp, vp, f32, f32, f32, i32,
+                                          vp, vp, vp, sz, vp]
+        L.attn_fp8_decode_fwd.restype = i32
         L.attn_check_slot_mapping_host.argtypes = [P(attn_desc), vp]
         L.attn_check_slot_mapping_host.restype = i32
         L.attn_status_str.argtypes = [i32]
@@ -245,6 +252,79 @@ def attn_check_slot_mapping_host(desc: attn_desc, slot_mapping: np.ndarray) -> i
                                                   a.ctypes.data_as(ctypes.c_void_p)))
 
 
+def _check_kv_rows(desc, key, value, dt, dev):
+    row = desc.num_kv_heads * desc.head_size
+    for name, t in (("key", key), ("value", value)):
+        if t.dtype != dt or t.device != dev:
+            raise TypeError(f"{name} must be {dt} on {dev}")
+        if tuple(t.shape) != (desc.num_tokens, desc.num_kv_heads, desc.head_size) or \
+                t.stride(2) != 1 or t.stride(1) != desc.head_size or t.stride(0) < row:
+            raise ValueError(f"{name} must be [num_tokens, num_kv_heads, head_size] with "
+                             "contiguous heads")
+
+
+def _fp8_cache_ok(kv_cache, desc, dev):
+    import torch
+    if kv_cache.device != dev or kv_cache.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError("the E4M3 cache must be a uint8 or float8_e4m3fn tensor on " + str(dev))
+    if not kv_cache.is_contiguous() or tuple(kv_cache.shape) != (
+            2, desc.num_blocks, desc.block_size, desc.num_kv_heads, desc.head_size):
+        raise ValueError("kv_cache shape does not match desc")
+
+
+def attn_kv_cache_write_fp8(desc: attn_desc, key, value, slot_mapping, k_scale: float,
+                            v_scale: float, kv_cache, stream=None) -> None:
+    """Queue the quantising write of bf16 K/V rows into an E4M3 cache (uint8 or
+    float8_e4m3fn tensor of the cache shape) at slot_mapping."""
+    import torch
+    dev = kv_cache.device
+    if dev.type != "cuda":
+        raise ValueError("attn_kv_cache_write_fp8 runs on a GPU device")
+    _check_kv_rows(desc, key, value, torch.bfloat16, dev)
+    _check_tensor("slot_mapping", slot_mapping, torch.int64, dev)
+    _fp8_cache_ok(kv_cache, desc, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = lib().attn_kv_cache_write_fp8(ctypes.byref(desc), _ptr(key), int(key.stride(0)),
+                                       _ptr(value), int(value.stride(0)), _ptr(slot_mapping),
+                                       float(k_scale), float(v_scale), _ptr(kv_cache),
+                                       ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_kv_cache_write_fp8")
+
+
+def attn_fp8_decode_fwd(desc: attn_desc, q, kv_cache, block_table, query_start_loc, seq_lens,
+                        scale: float, k_scale: float, v_scale: float, window: int, out, lse,
+                        workspace, stream=None) -> None:
+    """Queue decode attention (num_decodes == num_seqs) over an E4M3 cache; q / out bf16."""
+    import torch
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("attn_fp8_decode_fwd runs on a GPU device; q is on " + str(dev))
+    _check_tensor("q", q, torch.bfloat16, dev)
+    _check_tensor("out", out, torch.bfloat16, dev)
+    for n, t in (("block_table", block_table), ("query_start_loc", query_start_loc),
+                 ("seq_lens", seq_lens)):
+        _check_tensor(n, t, torch.int32, dev)
+    _check_tensor("lse", lse, torch.float32, dev, allow_none=True)
+    if workspace is not None:
+        _check_tensor("workspace", workspace, torch.uint8, dev)
+    _fp8_cache_ok(kv_cache, desc, dev)
+    if tuple(q.shape) != (desc.num_tokens, desc.num_heads, desc.head_size) or \
+            tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q/out shape does not match desc")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib().attn_fp8_decode_fwd(ctypes.byref(desc), _ptr(q), _ptr(kv_cache),
+                                   _ptr(block_table), _ptr(query_start_loc), _ptr(seq_lens),
+                                   float(scale), float(k_scale), float(v_scale), int(window),
+                                   _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                   ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fp8_decode_fwd")
+
+
 def attn_kv_cache_write(desc: attn_desc, key, value, slot_mapping, kv_cache,
                         stream=None) -> None:
     """Queue the write of the new tokens' K/V rows into kv_cache at slot_mapping.
@@ -258,14 +338,7 @@ def attn_kv_cache_write(desc: attn_desc, key, value, slot_mapping, kv_cache,
     if dev.type != "cuda":
         raise ValueError("attn_kv_cache_write runs on a GPU device; kv_cache is on " + str(dev))
     dt = torch.bfloat16 if desc.dtype == ATTN_BF16 else torch.float32
-    row = desc.num_kv_heads * desc.head_size
-    for name, t in (("key", key), ("value", value)):
-        if t.dtype != dt or t.device != dev:
-            raise TypeError(f"{name} must be {dt} on {dev}")
-        if tuple(t.shape) != (desc.num_tokens, desc.num_kv_heads, desc.head_size) or \
-                t.stride(2) != 1 or t.stride(1) != desc.head_size or t.stride(0) < row:
-            raise ValueError(f"{name} must be [num_tokens, num_kv_heads, head_size] with "
-                             "contiguous heads")
+    _check_kv_rows(desc, key, value, dt, dev)
     _check_tensor("slot_mapping", slot_mapping, torch.int64, dev)
     _check_tensor("kv_cache", kv_cache, dt, dev)
     if slot_mapping.numel() != desc.num_tokens:

@@ -385,6 +385,74 @@ attn_status attn_kv_cache_write(const attn_desc* desc, const void* key, int64_t 
                                                                                 : ATTN_ERR_HIP;
 }
 
+attn_status attn_kv_cache_write_fp8(const attn_desc* desc, const void* key,
+                                    int64_t key_row_stride, const void* value,
+                                    int64_t value_row_stride, const int64_t* slot_mapping,
+                                    float k_scale, float v_scale, void* kv_cache, void* stream) {
+  if (desc == nullptr) return ATTN_ERR_NULL;
+  const attn_desc& d = *desc;
+  if (d.num_tokens < 0 || d.num_kv_heads <= 0 || d.num_blocks < 0) return ATTN_ERR_SHAPE;
+  if (d.block_size <= 0 || d.block_size % 16 != 0) return ATTN_ERR_BLOCK_SIZE;
+  if (d.head_size != 64 && d.head_size != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d.dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;          // bf16 rows in, codes out
+  if (!(k_scale > 0.f) || !std::isfinite(k_scale) || !(v_scale > 0.f) || !std::isfinite(v_scale))
+    return ATTN_ERR_UNSUPPORTED;
+  const int64_t row = (int64_t)d.num_kv_heads * d.head_size;        // elements per token row
+  if (key_row_stride < row || value_row_stride < row) return ATTN_ERR_SHAPE;
+  if ((key_row_stride * 2) % 16 != 0 || (value_row_stride * 2) % 16 != 0) return ATTN_ERR_SHAPE;
+  if ((int64_t)d.num_tokens * 2 * (row / 16) / 256 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+  if (d.num_tokens == 0) return ATTN_OK;
+  if (key == nullptr || value == nullptr || slot_mapping == nullptr || kv_cache == nullptr)
+    return ATTN_ERR_NULL;
+  if ((uintptr_t)key % 16 != 0 || (uintptr_t)value % 16 != 0 || (uintptr_t)kv_cache % 16 != 0)
+    return ATTN_ERR_SHAPE;
+  attn::KvWriteParams p{};
+  p.key = key;
+  p.value = value;
+  p.slot_mapping = slot_mapping;
+  p.kv_cache = kv_cache;
+  p.num_tokens = d.num_tokens;
+  p.key_stride_bytes = key_row_stride * 2;
+  p.value_stride_bytes = value_row_stride * 2;
+  p.slot_bytes = row;                                               // one code per element
+  p.row_chunks = row / 16;
+  p.num_slots = (int64_t)d.num_blocks * d.block_size;
+  p.v_offset_bytes = p.num_slots * p.slot_bytes;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  return attn::launch_kv_write_fp8(p, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_fp8_decode_fwd(const attn_desc* desc, const void* q, const void* kv_cache,
+                                const int32_t* block_table, const int32_t* query_start_loc,
+                                const int32_t* seq_lens, float scale, float k_scale,
+                                float v_scale, int32_t window, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status s = check_desc(desc);
+  if (s != ATTN_OK) return s;
+  const attn_desc& d = *desc;
+  if (d.dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;            // q and out are bf16
+  if (d.num_decodes != d.num_seqs) return ATTN_ERR_UNSUPPORTED;     // decode rows only
+  if (!(scale > 0.f) || !std::isfinite(scale) || !(k_scale > 0.f) || !std::isfinite(k_scale) ||
+      !(v_scale > 0.f) || !std::isfinite(v_scale))
+    return ATTN_ERR_UNSUPPORTED;
+  if (d.num_seqs == 0 || d.num_tokens == 0) return ATTN_OK;
+  if (q == nullptr || kv_cache == nullptr || block_table == nullptr ||
+      query_start_loc == nullptr || seq_lens == nullptr || out == nullptr)
+    return ATTN_ERR_NULL;
+  const int64_t max_parts = decode_max_parts(&d, window);
+  const size_t need = workspace_for(&d, max_parts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  // k_scale multiplies every score: fold it into the softmax scale
+  const attn::PrefillParams pp = prefill_params(d, q, kv_cache, block_table, query_start_loc,
+                                                seq_lens, scale * k_scale, 1, window, out, lse);
+  attn::DecodeParams dp = decode_params(d, pp, max_parts, static_cast<float*>(workspace));
+  dp.v_scale = v_scale;
+  return attn::launch_decode_fp8(dp, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 attn_status attn_check_slot_mapping_host(const attn_desc* desc, const int64_t* slot_mapping) {
   if (desc == nullptr) return ATTN_ERR_NULL;
   const attn_desc& d = *desc;

@@ -16,6 +16,8 @@
 //   * V rows are copied into a wave-private LDS tile and read back transposed with
 //     ds_read_b64_tr_b16 as the A operand of O^T += V^T . P^T;
 //   * the 4 waves' (max, sum, O) are combined through LDS at the end.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -25,7 +27,21 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kChunk = 32;       // keys per wave iteration
 
-template <int D>
+// 8 E4M3 codes (two 32-bit words) -> 8 bf16 values, exactly (every E4M3 value is a bf16
+// value; v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts two codes, checked on gfx950 for all
+// 256 codes).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// FP8 = true: the cache holds E4M3 codes (one byte per element) with per-tensor scales; the
+// host folds k_scale into p.scale and the kernel multiplies the output by p.v_scale.
+template <int D, bool FP8>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams p) {
   constexpr int RS = D + 16;           // LDS row stride (bf16) of a V chunk
   constexpr int KC = D / 32;
@@ -81,15 +97,19 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   for (int i = tid; i < n_blk; i += 256) sBlk[i] = bt[b_first + i];
 
   const __bf16* __restrict__ q = static_cast<const __bf16*>(p.q);
-  const __bf16* __restrict__ kcache = static_cast<const __bf16*>(p.kv);
-  const __bf16* __restrict__ vcache = kcache + p.v_offset;
+  typedef typename std::conditional<FP8, uint8_t, __bf16>::type kv_t;
+  const kv_t* __restrict__ kcache = static_cast<const kv_t*>(p.kv);
+  const kv_t* __restrict__ vcache = kcache + p.v_offset;
 
-  // Q^T (B operand): lane (G, li) holds q head h0 + li, d = 32c + 8G .. +7
+  // Q^T (B operand): lane (G, li) holds q head h0 + li at the d values its K operand holds:
+  // d = 32c + 8G .. +7 (bf16), or d = (D/4)G + 8c .. +7 for E4M3 K, where each lane reads one
+  // contiguous D/4-byte strip of the row (any fixed order of d is the same dot product)
   bf16x8 qf[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
+    const int d0 = FP8 ? (D / 4) * G + 8 * c : 32 * c + 8 * G;
     qf[c] = li < nh ? *reinterpret_cast<const bf16x8*>(
-                          q + ((int64_t)tok * p.num_heads + h0 + li) * D + 32 * c + 8 * G)
+                          q + ((int64_t)tok * p.num_heads + h0 + li) * D + d0)
                     : bf16x8{};
   }
 
@@ -108,9 +128,13 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   const int v_chunk = lane % TPR;
   __syncthreads();   // sBlk ready
 
+  // raw K / V of one chunk: bf16 K as MFMA operands, E4M3 K as each lane's D/4-byte strip
+  // (D/64 16-byte words); V as 16 bytes (bf16) or 8 bytes (E4M3) per lane and instruction
+  constexpr int KW = FP8 ? D / 64 : KC;
+  typedef typename std::conditional<FP8, u32x2, u32x4>::type vword_t;
   struct Chunk {
-    u32x4 k[2][KC];
-    u32x4 v[NV];
+    u32x4 k[2][KW];
+    vword_t v[NV];
   };
   // Element offset of the first row of the 16-key group starting at key g0 (clamped to the
   // last visible group, so every load below reads a valid row of this request). A 16-key
@@ -135,16 +159,22 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
     for (int t2 = 0; t2 < 2; ++t2) {
       int g0;
       const uint64_t base = group_off(kb + 16 * t2, &g0);
-      const __bf16* src = kcache + base + (uint32_t)(min(li, last_key - g0) * kv_row + 8 * G);
+      if constexpr (FP8) {
+        const kv_t* src = kcache + base + (uint32_t)(min(li, last_key - g0) * kv_row + (D / 4) * G);
 #pragma unroll
-      for (int c = 0; c < KC; ++c) ch.k[t2][c] = *reinterpret_cast<const u32x4*>(src + 32 * c);
+        for (int c = 0; c < KW; ++c) ch.k[t2][c] = *reinterpret_cast<const u32x4*>(src + 16 * c);
+      } else {
+        const kv_t* src = kcache + base + (uint32_t)(min(li, last_key - g0) * kv_row + 8 * G);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) ch.k[t2][c] = *reinterpret_cast<const u32x4*>(src + 32 * c);
+      }
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int row = j * RPI + v_row;                 // row in the chunk; its 16-key group
       int g0;                                          // is uniform across the instruction
       const uint64_t base = group_off(kb + (j * RPI / 16) * 16, &g0);
-      ch.v[j] = *reinterpret_cast<const u32x4*>(
+      ch.v[j] = *reinterpret_cast<const vword_t*>(
           vcache + base + (uint32_t)(min(row % 16, last_key - g0) * kv_row + 8 * v_chunk));
     }
   };
@@ -159,15 +189,25 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   auto consume = [&](Chunk& ch, int ci) {
     const int kb = c_base + (c_first + ci) * kChunk;
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-      *reinterpret_cast<u32x4*>(&sVw[(j * RPI + v_row) * RS + 8 * v_chunk]) = ch.v[j];
+    for (int j = 0; j < NV; ++j) {
+      bf16x8 vv;
+      if constexpr (FP8) vv = fp8x8_to_bf16x8(ch.v[j][0], ch.v[j][1]);
+      else vv = __builtin_bit_cast(bf16x8, ch.v[j]);
+      *reinterpret_cast<bf16x8*>(&sVw[(j * RPI + v_row) * RS + 8 * v_chunk]) = vv;
+    }
     floatx4 sc[2];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < KC; ++c)
-        acc = mfma16x16x32(__builtin_bit_cast(bf16x8, ch.k[t2][c]), qf[c], acc);
+      for (int c = 0; c < KC; ++c) {
+        bf16x8 ka;
+        if constexpr (FP8)
+          ka = fp8x8_to_bf16x8(ch.k[t2][c / 2][2 * (c % 2)], ch.k[t2][c / 2][2 * (c % 2) + 1]);
+        else
+          ka = __builtin_bit_cast(bf16x8, ch.k[t2][c]);
+        acc = mfma16x16x32(ka, qf[c], acc);
+      }
       sc[t2] = acc;
     }
     if (ci + 2 < n_chunks) load_chunk(ch, kb + 2 * kChunk);
@@ -258,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
     float a = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) a += wgt[ww] * sO[(ww * 16 + hh) * OS + d0 + x];
-    acc[x] = a * inv;
+    acc[x] = FP8 ? a * inv * p.v_scale : a * inv;
   }
   const float lse_part = L > 0.f ? p.scale * M + __logf(L) : -INFINITY;
   const int hq = h0 + hh;
@@ -327,12 +367,12 @@ __global__ __launch_bounds__(64) void lse_merge_kernel(const DecodeParams p) {
   if (p.lse != nullptr && lane == 0) p.lse[row] = L;
 }
 
-template <int D>
+template <int D, bool FP8>
 hipError_t launch(const DecodeParams& p, hipStream_t stream) {
   const int group = p.num_heads / p.num_kv_heads;
   const int head_groups = (group + 15) / 16;
   const dim3 grid(p.num_kv_heads * head_groups, p.max_parts, p.num_decodes);
-  hipLaunchKernelGGL(decode_split_kernel<D>, grid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((decode_split_kernel<D, FP8>), grid, dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (p.max_parts <= 1 && p.pre_o == nullptr)) return e;
   hipLaunchKernelGGL(lse_merge_kernel<D>, dim3(p.num_heads, p.num_decodes), dim3(kWave), 0,
@@ -344,7 +384,12 @@ hipError_t launch(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
   if (p.num_decodes <= 0) return hipSuccess;
-  return p.head_size == 64 ? launch<64>(p, stream) : launch<128>(p, stream);
+  return p.head_size == 64 ? launch<64, false>(p, stream) : launch<128, false>(p, stream);
+}
+
+hipError_t launch_decode_fp8(const DecodeParams& p, hipStream_t stream) {
+  if (p.num_decodes <= 0) return hipSuccess;
+  return p.head_size == 64 ? launch<64, true>(p, stream) : launch<128, true>(p, stream);
 }
 
 }  // namespace attn

@@ -59,6 +59,8 @@ struct DecodeParams {
   int32_t window;
   float scale;
   uint64_t group_recip;         // ceil(2^32 / (block_size / 16)), as in PrefillParams
+  float v_scale;                // E4M3 cache only: V dequantisation scale (k_scale is folded
+                                // into scale by the host)
   // Cascade suffix pass (zero / null for a plain call):
   int32_t kv_skip_blocks;       // as in PrefillParams
   const float* pre_o;           // non-null: a partial result over the prefix, fp32
@@ -101,13 +103,17 @@ struct KvWriteParams {
   int64_t slot_bytes;           // bytes of one slot = one token's row
   int64_t num_slots;            // num_blocks * block_size
   int64_t v_offset_bytes;       // bytes from the K half to the V half
+  float k_scale, v_scale;       // E4M3 cache only: code = E4M3(x / scale)
 };
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t stream);
+// E4M3 cache from bf16 rows: row_chunks counts 16-code chunks (slot_bytes = codes per row)
+hipError_t launch_kv_write_fp8(const KvWriteParams& p, hipStream_t stream);
 hipError_t launch_prefix_slices_merge(const PrefixMergeParams& p, int head_size,
                                       hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeParams& p, hipStream_t stream);   // E4M3 cache
 
 }  // namespace attn

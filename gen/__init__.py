@@ -265,6 +265,15 @@ def to_numpy_f64(t) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
+def subset_meta(batch: Batch, requests: Sequence[int]) -> Batch:
+    """The same block pool and cache, with the metadata of ``requests`` only (in order)."""
+    r = list(requests)
+    return dataclasses.replace(batch, name=batch.name + "-requests",
+                               query_lens=batch.query_lens[r].copy(),
+                               seq_lens=batch.seq_lens[r].copy(),
+                               block_table=batch.block_table[r].copy())
+
+
 def subset(batch: Batch, requests: Sequence[int], q, kv):
     """A smaller batch holding only ``requests`` (in the given order), with its own compact
     block pool and remapped table; returns (sub_batch, q_sub, kv_sub) as host torch tensors.

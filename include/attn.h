@@ -233,6 +233,41 @@ attn_status attn_kv_cache_write(const attn_desc* desc, const void* key, int64_t 
                                 const int64_t* slot_mapping, void* kv_cache, void* stream);
 
 /*
+ * FP8 KV cache (E4M3). The Triton Attention section of [OTH] names an FP8 KV cache and [RBLN]
+ * states which of its modes support one; neither fixes the format or the scaling, so this
+ * library reads it as: OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * subnormals, NaN = exponent and mantissa all ones, no infinity, largest magnitude 448), one
+ * fp32 scale per tensor for K and one for V, a code c standing for value(c) * scale. The
+ * cache has the usual shape [2][num_blocks][block_size][num_kv_heads][head_size], one byte per
+ * element.
+ *
+ * attn_kv_cache_write_fp8: as attn_kv_cache_write, with bf16 key / value rows (desc->dtype
+ * must be ATTN_BF16) stored as the code nearest to x / scale (quotient in fp32, ties to even,
+ * magnitudes beyond 448 saturated to 448; a NaN input gives a NaN code). Errors: those of
+ * attn_kv_cache_write; ATTN_ERR_UNSUPPORTED for another dtype or a scale that is not finite
+ * and > 0.
+ */
+attn_status attn_kv_cache_write_fp8(const attn_desc* desc, const void* key,
+                                    int64_t key_row_stride, const void* value,
+                                    int64_t value_row_stride, const int64_t* slot_mapping,
+                                    float k_scale, float v_scale, void* kv_cache, void* stream);
+
+/*
+ * attn_fp8_decode_fwd: attn_varlen_fwd for a batch of decode rows only (num_decodes ==
+ * num_seqs, query_len 1 each) over an E4M3 cache: the same exact attention with K and V
+ * dequantised (value(code) * k_scale, value(code) * v_scale). q and out are bf16 (desc->dtype
+ * ATTN_BF16), lse fp32; the codes are converted to bf16 exactly (every E4M3 value is a bf16
+ * value) and k_scale / v_scale are applied to the scores and the output in fp32. Workspace:
+ * attn_workspace_bytes(desc). Errors: those of attn_varlen_fwd; ATTN_ERR_UNSUPPORTED for
+ * num_decodes != num_seqs, a dtype other than ATTN_BF16, or scales that are not finite and > 0.
+ */
+attn_status attn_fp8_decode_fwd(const attn_desc* desc, const void* q, const void* kv_cache,
+                                const int32_t* block_table, const int32_t* query_start_loc,
+                                const int32_t* seq_lens, float scale, float k_scale,
+                                float v_scale, int32_t window, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_check_slot_mapping_host: every slot of the host array slot_mapping[num_tokens] is
  * negative (padding) or below num_blocks * block_size, and the non-negative slots are
  * distinct. Returns ATTN_OK, ATTN_ERR_METADATA, ATTN_ERR_NULL, ATTN_ERR_SHAPE or

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def _declared():
     src = open(os.path.join(ROOT, "include", "attn.h")).read()
-    return sorted(set(re.findall(r"^\S[^\n(]*?\b(attn_[a-z_]+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^\S[^\n(]*?\b(attn_[a-z0-9_]+)\s*\(", src, re.M)))
 
 
 def test_header_declares_the_python_names():
@@ -256,3 +256,36 @@ def test_kv_write_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         A.attn_kv_cache_write(_desc(), k, k, torch.zeros(5, dtype=torch.int64),
                               torch.zeros(2, 8, 16, 2, 128, dtype=torch.bfloat16))
+
+
+# ---------------------------------------------------------------- FP8 (E4M3) cache
+def _fp8_decode(desc, scale=0.1, ks=0.02, vs=0.03, window=0, ws=None, ws_bytes=0, q=FAKE):
+    return A.lib().attn_fp8_decode_fwd(ctypes.byref(desc), q, FAKE, FAKE, FAKE, FAKE, scale, ks,
+                                       vs, window, FAKE, None, ws, ws_bytes, None)
+
+
+def test_fp8_decode_argument_errors():
+    dec = dict(num_seqs=2, num_tokens=2, num_decodes=2, max_query_len=1)
+    d = _desc(**dec)
+    assert _fp8_decode(_desc()) == A.ATTN_ERR_UNSUPPORTED          # prefill rows present
+    assert _fp8_decode(_desc(dtype=A.ATTN_F32, **dec)) == A.ATTN_ERR_UNSUPPORTED
+    assert _fp8_decode(d, ks=0.0) == A.ATTN_ERR_UNSUPPORTED
+    assert _fp8_decode(d, vs=float("inf")) == A.ATTN_ERR_UNSUPPORTED
+    assert _fp8_decode(d, scale=-1.0) == A.ATTN_ERR_UNSUPPORTED
+    assert _fp8_decode(d, q=None) == A.ATTN_ERR_NULL
+    need = A.attn_workspace_bytes(d)
+    assert _fp8_decode(d, ws=FAKE, ws_bytes=need - 1) == A.ATTN_ERR_WORKSPACE
+    assert _fp8_decode(_desc(block_size=24, **dec)) == A.ATTN_ERR_BLOCK_SIZE
+
+
+def test_fp8_write_argument_errors():
+    def w(desc, ks=0.02, vs=0.03, stride=256):
+        return A.lib().attn_kv_cache_write_fp8(ctypes.byref(desc), FAKE, stride, FAKE, stride,
+                                               FAKE, ks, vs, FAKE, None)
+    assert w(_desc(dtype=A.ATTN_F32)) == A.ATTN_ERR_UNSUPPORTED
+    assert w(_desc(), ks=-1.0) == A.ATTN_ERR_UNSUPPORTED
+    assert w(_desc(), vs=float("nan")) == A.ATTN_ERR_UNSUPPORTED
+    assert w(_desc(), stride=100) == A.ATTN_ERR_SHAPE
+    assert w(_desc(), stride=260) == A.ATTN_ERR_SHAPE                # 520 bytes
+    assert w(_desc(head_size=96)) == A.ATTN_ERR_UNSUPPORTED
+    assert w(_desc(num_tokens=0)) == A.ATTN_OK
