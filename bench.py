@@ -337,6 +337,62 @@ def fp8_decode_report(dev, seed):
                               "tokens_per_s": round(keys / (ms / 1e3), 1)}), flush=True)
 
 
+def schedule_report(dev, seed):
+    """Prefill calls with the device-built work schedule (attn_varlen_fwd_scheduled) against
+    the plain grid (attn_varlen_fwd), on the prefill workloads and on a skewed varlen batch.
+    The schedule is built once per batch and mask (outside the timed calls, as it would be
+    reused by every layer); its build time is reported separately."""
+    import torch
+    import exact_softmax_attention_paged_amd as A
+    import gen
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in (2, 3):
+        b = gen.config(k)
+        cases.append((gen.CONFIG_NAMES[k], b, b.passes[0], k))
+    b5 = gen.config(5, seed=seed)
+    b5p = gen.subset_meta(b5, list(range(b5.num_decodes, b5.num_seqs)))
+    for li, pas in enumerate(b5.passes):
+        cases.append((f"mixed-long-context prefill requests, pass {li}", b5p, pas, 5))
+    sl = rng.integers(64, 8192, size=24, endpoint=True)
+    bsk = gen.make_batch("skewed", num_heads=32, num_kv_heads=8, head_size=128, block_size=16,
+                         dtype="bf16", query_lens=sl, seq_lens=sl, passes=[(True, 0)],
+                         seed=seed)
+    cases.append(("skewed varlen causal: 24 requests, ql = sl ~ U[64, 8192], 32q/8kv, d128",
+                  bsk, (True, 0), seed))
+    for name, b, (causal, window), s in cases:
+        q = gen.make_q(b, s, dev)
+        kv = gen.make_kv(b, s, dev)
+        bt, qsl, sl_d = (torch.from_numpy(x).to(dev) for x in (b.block_table,
+                                                               b.query_start_loc, b.seq_lens))
+        desc = A.make_desc(num_seqs=b.num_seqs, num_tokens=b.num_tokens,
+                           num_decodes=b.num_decodes, max_query_len=b.max_query_len,
+                           max_seq_len=b.max_seq_len, num_heads=b.num_heads,
+                           num_kv_heads=b.num_kv_heads, head_size=b.head_size,
+                           num_blocks=b.num_blocks, block_size=b.block_size,
+                           max_blocks_per_seq=b.max_blocks_per_seq, dtype=A.ATTN_BF16)
+        out = torch.empty_like(q)
+        lse = torch.empty(b.num_tokens, b.num_heads, dtype=torch.float32, device=dev)
+        sched = torch.empty(A.attn_schedule_bytes(desc) // 4, dtype=torch.int32, device=dev)
+        reps = 5 if b.num_tokens > 10000 else 50
+        t_build = _time_ms(lambda: A.attn_build_schedule(desc, qsl, sl_d, causal, window, sched),
+                           reps)
+        tp = _time_ms(lambda: A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl_d, b.scale, causal,
+                                                window, out, lse, None), reps)
+        ts = _time_ms(lambda: A.attn_varlen_fwd_scheduled(desc, q, kv, bt, qsl, sl_d, b.scale,
+                                                          causal, window, out, lse, None, sched),
+                      reps)
+        import oracle  # visible-pair count of the definition, for the flop rate
+        f = 4.0 * b.head_size * b.num_heads * oracle.flops_visible_pairs(
+            b.query_lens, b.seq_lens, causal, window)
+        print(json.dumps({"report": "schedule", "batch": name, "causal": causal,
+                          "window": window, "plain_ms": round(tp, 4),
+                          "scheduled_ms": round(ts, 4), "speedup": round(tp / ts, 3),
+                          "schedule_build_ms": round(t_build, 4),
+                          "plain_tflops": round(f / (tp / 1e3) / 1e12, 1),
+                          "scheduled_tflops": round(f / (ts / 1e3) / 1e12, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -349,7 +405,7 @@ def main():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/prefill_traffic.json from two rocprofv3 --pmc runs")
     ap.add_argument("--record-command", default="", help="command line stored with the record")
-    ap.add_argument("--report", choices=["cascade", "kv-write", "fp8-decode"],
+    ap.add_argument("--report", choices=["cascade", "kv-write", "fp8-decode", "schedule"],
                     help="instead of the headline step, time one of the next-step paths "
                          "against the plain path and print one JSON line per batch")
     args = ap.parse_args()
@@ -380,6 +436,9 @@ def main():
         return
     if args.report == "fp8-decode":
         fp8_decode_report(dev, args.seed)
+        return
+    if args.report == "schedule":
+        schedule_report(dev, args.seed)
         return
     batch = gen.config(5, seed=args.seed)
     nd = batch.num_decodes

@@ -24,7 +24,8 @@ ATTN_BF16, ATTN_F32 = 0, 1
 EXPORTED = ("attn_workspace_bytes", "attn_varlen_fwd", "attn_check_metadata_host",
             "attn_cascade_workspace_bytes", "attn_cascade_fwd", "attn_check_cascade_host",
             "attn_kv_cache_write", "attn_check_slot_mapping_host", "attn_kv_cache_write_fp8",
-            "attn_fp8_decode_fwd", "attn_status_str")
+            "attn_fp8_decode_fwd", "attn_schedule_bytes", "attn_build_schedule",
+            "attn_varlen_fwd_scheduled", "attn_status_str")
 
 
 class attn_desc(ctypes.Structure):
@@ -78,6 +79,13 @@ def lib():
         L.attn_fp8_decode_fwd.argtypes = [P(attn_desc), vp, vp, vp, vp, vp, f32, f32, f32, i32,
                                           vp, vp, vp, sz, vp]
         L.attn_fp8_decode_fwd.restype = i32
+        L.attn_schedule_bytes.argtypes = [P(attn_desc), P(sz)]
+        L.attn_schedule_bytes.restype = i32
+        L.attn_build_schedule.argtypes = [P(attn_desc), vp, vp, i32, i32, vp, sz, vp]
+        L.attn_build_schedule.restype = i32
+        L.attn_varlen_fwd_scheduled.argtypes = [P(attn_desc), vp, vp, vp, vp, vp, f32, i32, i32,
+                                                vp, vp, vp, sz, vp, sz, vp]
+        L.attn_varlen_fwd_scheduled.restype = i32
         L.attn_check_slot_mapping_host.argtypes = [P(attn_desc), vp]
         L.attn_check_slot_mapping_host.restype = i32
         L.attn_status_str.argtypes = [i32]
@@ -353,3 +361,51 @@ def attn_kv_cache_write(desc: attn_desc, key, value, slot_mapping, kv_cache,
                                    _ptr(kv_cache), ctypes.c_void_p(stream.cuda_stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_kv_cache_write")
+
+
+def attn_schedule_bytes(desc: attn_desc) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().attn_schedule_bytes(ctypes.byref(desc), ctypes.byref(n))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_schedule_bytes")
+    return int(n.value)
+
+
+def attn_build_schedule(desc: attn_desc, query_start_loc, seq_lens, causal: bool, window: int,
+                        schedule, stream=None) -> None:
+    """Queue the build of the prefill work schedule into ``schedule`` (int32 device tensor of
+    at least attn_schedule_bytes(desc) / 4 elements)."""
+    import torch
+    dev = schedule.device
+    if dev.type != "cuda":
+        raise ValueError("attn_build_schedule runs on a GPU device")
+    for n, t in (("query_start_loc", query_start_loc), ("seq_lens", seq_lens),
+                 ("schedule", schedule)):
+        _check_tensor(n, t, torch.int32, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = lib().attn_build_schedule(ctypes.byref(desc), _ptr(query_start_loc), _ptr(seq_lens),
+                                   1 if causal else 0, int(window), _ptr(schedule),
+                                   schedule.numel() * 4, ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_build_schedule")
+
+
+def attn_varlen_fwd_scheduled(desc: attn_desc, q, kv_cache, block_table, query_start_loc,
+                              seq_lens, scale: float, causal: bool, window: int, out, lse,
+                              workspace, schedule, stream=None) -> None:
+    """attn_varlen_fwd with the prefill rows dispatched in the order of ``schedule``."""
+    import torch
+    _check_call("attn_varlen_fwd_scheduled", desc, q, kv_cache, block_table, query_start_loc,
+                seq_lens, out, lse, workspace)
+    _check_tensor("schedule", schedule, torch.int32, q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib().attn_varlen_fwd_scheduled(
+        ctypes.byref(desc), _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(query_start_loc),
+        _ptr(seq_lens), float(scale), 1 if causal else 0, int(window), _ptr(out), _ptr(lse),
+        _ptr(workspace), ws_bytes, _ptr(schedule), schedule.numel() * 4,
+        ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_varlen_fwd_scheduled")

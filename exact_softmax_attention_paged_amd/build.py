@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = ["attn_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip",
-           "cascade_bf16.hip", "kv_write.hip"]
+           "cascade_bf16.hip", "kv_write.hip", "schedule.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the device code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -149,6 +149,13 @@ attn::DecodeParams decode_params(const attn_desc& d, const attn::PrefillParams& 
   return dp;
 }
 
+// Prefill work schedule: one int32 count plus one int32 per (prefill request, q tile) slot.
+int64_t schedule_max_qtiles(const attn_desc* d) { return ceil_div(d->max_query_len, 256); }
+size_t schedule_bytes_for(const attn_desc* d) {
+  const int64_t slots = (int64_t)(d->num_seqs - d->num_decodes) * schedule_max_qtiles(d);
+  return round256((1 + slots) * 4);
+}
+
 // Checks of a cascade call that need nothing but the descriptor and the prefix length.
 attn_status check_cascade(const attn_desc* d, int32_t common_prefix_len) {
   const attn_status s = check_desc(d);
@@ -318,6 +325,82 @@ attn_status attn_check_cascade_host(const attn_desc* desc, const int32_t* block_
     for (int64_t b = 0; b < nb; ++b)
       if (block_table[(int64_t)r * d.max_blocks_per_seq + b] != block_table[b])
         return ATTN_ERR_METADATA;
+  }
+  return ATTN_OK;
+}
+
+attn_status attn_schedule_bytes(const attn_desc* desc, size_t* bytes) {
+  if (bytes == nullptr) return ATTN_ERR_NULL;
+  const attn_status s = check_desc(desc);
+  if (s != ATTN_OK) return s;
+  if ((int64_t)(desc->num_seqs - desc->num_decodes) * schedule_max_qtiles(desc) *
+          desc->num_heads >= ((int64_t)1 << 31))
+    return ATTN_ERR_SHAPE;
+  *bytes = schedule_bytes_for(desc);
+  return ATTN_OK;
+}
+
+attn_status attn_build_schedule(const attn_desc* desc, const int32_t* query_start_loc,
+                                const int32_t* seq_lens, int32_t causal, int32_t window,
+                                int32_t* schedule, size_t schedule_bytes, void* stream) {
+  size_t need = 0;
+  const attn_status s = attn_schedule_bytes(desc, &need);
+  if (s != ATTN_OK) return s;
+  if (window > 0 && !causal) return ATTN_ERR_UNSUPPORTED;
+  if (schedule == nullptr || schedule_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (desc->num_seqs > desc->num_decodes && (query_start_loc == nullptr || seq_lens == nullptr))
+    return ATTN_ERR_NULL;
+  attn::ScheduleParams sp{};
+  sp.qsl = query_start_loc;
+  sp.seq_lens = seq_lens;
+  sp.schedule = schedule;
+  sp.seq_begin = desc->num_decodes;
+  sp.num_seqs = desc->num_seqs - desc->num_decodes;
+  sp.max_qtiles = (int32_t)schedule_max_qtiles(desc);
+  sp.causal = causal ? 1 : 0;
+  sp.window = window > 0 ? window : 0;
+  return attn::launch_prefill_schedule(sp, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_varlen_fwd_scheduled(const attn_desc* desc, const void* q, const void* kv_cache,
+                                      const int32_t* block_table,
+                                      const int32_t* query_start_loc, const int32_t* seq_lens,
+                                      float scale, int32_t causal, int32_t window, void* out,
+                                      float* lse, void* workspace, size_t workspace_bytes,
+                                      const int32_t* schedule, size_t schedule_bytes,
+                                      void* stream) {
+  attn_status s = check_desc(desc);
+  if (s != ATTN_OK) return s;
+  const attn_desc& d = *desc;
+  if (d.dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  size_t need_sched = 0;
+  s = attn_schedule_bytes(desc, &need_sched);
+  if (s != ATTN_OK) return s;
+  if (window > 0 && !causal) return ATTN_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (d.num_seqs == 0 || d.num_tokens == 0) return ATTN_OK;
+  if (q == nullptr || kv_cache == nullptr || block_table == nullptr ||
+      query_start_loc == nullptr || seq_lens == nullptr || out == nullptr)
+    return ATTN_ERR_NULL;
+  if (schedule == nullptr || schedule_bytes < need_sched) return ATTN_ERR_WORKSPACE;
+  const int64_t max_parts = decode_max_parts(&d, window);
+  const size_t need = workspace_for(&d, max_parts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  attn::PrefillParams pp = prefill_params(d, q, kv_cache, block_table, query_start_loc,
+                                          seq_lens, scale, causal, window, out, lse);
+  if (d.num_decodes > 0) {
+    const attn::DecodeParams dp =
+        decode_params(d, pp, max_parts, static_cast<float*>(workspace));
+    if (attn::launch_decode_bf16(dp, st) != hipSuccess) return ATTN_ERR_HIP;
+  }
+  if (d.num_seqs > d.num_decodes) {
+    pp.seq_begin = d.num_decodes;
+    pp.num_seqs = d.num_seqs - d.num_decodes;
+    pp.schedule = schedule;
+    pp.max_qtiles = (int32_t)schedule_max_qtiles(&d);
+    if (attn::launch_prefill_bf16(pp, st) != hipSuccess) return ATTN_ERR_HIP;
   }
   return ATTN_OK;
 }

@@ -38,6 +38,9 @@ struct PrefillParams {
   int32_t single_slice;
   int64_t slice_stride;         // (token, head) rows between slices of out_f32 and lse
   float* out_f32;               // non-null: write O (normalised) in fp32 here, not to out
+  const int32_t* schedule;      // non-null: grid x = item slot * num_heads + q head, items
+                                // from a prefill schedule (see ScheduleParams)
+  int32_t max_qtiles;           // q tiles per request in the schedule's item numbering
   const float* init_o;          // non-null: start each row from a partial result over
   const float* init_lse;        // earlier keys, fp32 [token][head][d] and [token][head]
 };
@@ -106,7 +109,18 @@ struct KvWriteParams {
   float k_scale, v_scale;       // E4M3 cache only: code = E4M3(x / scale)
 };
 
+// Prefill work schedule: items (request, 256-row q tile) of requests
+// [seq_begin, seq_begin + num_seqs), sorted by their number of 64-key tiles, longest first.
+struct ScheduleParams {
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  int32_t* schedule;            // [0] = item count, then the items
+  int32_t seq_begin, num_seqs, max_qtiles;
+  int32_t causal, window;
+};
+
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_prefill_schedule(const ScheduleParams& p, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t stream);
 // E4M3 cache from bf16 rows: row_chunks counts 16-code chunks (slot_bytes = codes per row)
 hipError_t launch_kv_write_fp8(const KvWriteParams& p, hipStream_t stream);

@@ -104,8 +104,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
 
   const bool single = p.single_ql > 0;          // cascade prefix pass: one sequence
   const int group = p.num_heads / p.num_kv_heads;
-  const int r = single ? 0 : p.seq_begin + blockIdx.z;
-  const int qt = gridDim.x - 1 - blockIdx.x;   // longest (causal) tiles are dispatched first
+  int r, qt, hq_grid;
+  if (p.schedule != nullptr) {
+    // item slot blockIdx.x / num_heads of the schedule (sorted longest first), q head
+    // blockIdx.x % num_heads; slots past the item count have nothing to do
+    const int slot = blockIdx.x / p.num_heads;
+    if (slot >= p.schedule[0]) return;
+    const int e = p.schedule[1 + slot];
+    r = p.seq_begin + e / p.max_qtiles;
+    qt = e % p.max_qtiles;
+    hq_grid = blockIdx.x % p.num_heads;
+  } else {
+    r = single ? 0 : p.seq_begin + blockIdx.z;
+    qt = gridDim.x - 1 - blockIdx.x;           // longest (causal) tiles are dispatched first
+    hq_grid = blockIdx.y;
+  }
   const int q_start = single ? 0 : p.qsl[r];
   // query rows of this workgroup's sequence: its tokens, or in the prefix pass the
   // (token, q head) pairs of one GQA group
@@ -114,7 +127,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   // keys of this pass: [0, sl) after skipping kv_skip_blocks leading blocks
   const int sl = single ? p.single_sl : p.seq_lens[r] - p.kv_skip_blocks * p.block_size;
   const int cl = sl - ql;
-  const int kvh = single ? (int)blockIdx.y : (int)blockIdx.y / group;
+  const int kvh = single ? hq_grid : hq_grid / group;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave index, uniform
@@ -132,7 +145,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   const int my_row = min(wrow0 + lq, ql - 1);            // rows past ql: any valid row
   const int64_t my_th = single
       ? (int64_t)(my_row / group) * p.num_heads + kvh * group + my_row % group
-      : (int64_t)(q_start + my_row) * p.num_heads + blockIdx.y;
+      : (int64_t)(q_start + my_row) * p.num_heads + hq_grid;
 
   // ---- Q^T (B operand): lane l holds query lq, d = 16c + 8h .. +7
   bf16x8 qf[KC];
@@ -442,7 +455,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
 template <int D, bool CAUSAL, bool WINDOW>
 hipError_t launch(const PrefillParams& p, hipStream_t stream) {
   dim3 grid((p.max_query_len + kBR - 1) / kBR, p.num_heads, p.num_seqs);
-  if (p.single_ql > 0) {            // prefix pass: (token, head) rows per kv head, key slices
+  if (p.schedule != nullptr) {       // one workgroup per (schedule slot, q head)
+    grid = dim3((unsigned)((int64_t)p.num_seqs * p.max_qtiles * p.num_heads), 1, 1);
+  } else if (p.single_ql > 0) {            // prefix pass: (token, head) rows per kv head, key slices
     const int rows = p.single_ql * (p.num_heads / p.num_kv_heads);
     const int slices = p.single_slice > 0 ? (p.single_sl + p.single_slice - 1) / p.single_slice : 1;
     grid = dim3((rows + kBR - 1) / kBR, p.num_kv_heads, slices);

@@ -275,6 +275,40 @@ attn_status attn_fp8_decode_fwd(const attn_desc* desc, const void* q, const void
  */
 attn_status attn_check_slot_mapping_host(const attn_desc* desc, const int64_t* slot_mapping);
 
+/*
+ * Prefill work schedule built ahead of the attention call ([FA] FA3 section: the work
+ * distribution is computed before the kernel and kept in a preallocated int32 buffer, so that
+ * the launch is the same under graph capture). The schedule lists the batch's prefill work
+ * items - (request, 256-row query tile) for requests [num_decodes, num_seqs) - sorted by the
+ * number of 64-key tiles each must read (given causal / window), longest first; the scheduled
+ * call dispatches its prefill workgroups in that order across the whole batch and launches
+ * none for tiles past a request's last query row. A schedule depends only on
+ * query_start_loc, seq_lens, causal and window, so one build serves every layer of a batch.
+ *
+ * attn_schedule_bytes: bytes of the schedule buffer: 4 * (1 + (num_seqs - num_decodes) *
+ *   ceil(max_query_len / 256)), rounded up to 256. Errors: ATTN_ERR_NULL and the descriptor
+ *   errors of attn_varlen_fwd; ATTN_ERR_SHAPE when the scheduled grid would exceed 2^31
+ *   workgroups.
+ * attn_build_schedule: queue the device kernel that writes the schedule (int32; element 0 is
+ *   the item count, then the items) for the device metadata query_start_loc / seq_lens.
+ *   Errors: those of attn_schedule_bytes; ATTN_ERR_WORKSPACE when schedule is NULL or
+ *   schedule_bytes too small; ATTN_ERR_UNSUPPORTED for window > 0 without causal.
+ * attn_varlen_fwd_scheduled: attn_varlen_fwd (bf16 only) whose prefill rows follow a schedule
+ *   built for the same descriptor, metadata, causal and window (not checked: it would need a
+ *   device-to-host synchronisation). The results are identical to attn_varlen_fwd's.
+ */
+attn_status attn_schedule_bytes(const attn_desc* desc, size_t* bytes);
+attn_status attn_build_schedule(const attn_desc* desc, const int32_t* query_start_loc,
+                                const int32_t* seq_lens, int32_t causal, int32_t window,
+                                int32_t* schedule, size_t schedule_bytes, void* stream);
+attn_status attn_varlen_fwd_scheduled(const attn_desc* desc, const void* q, const void* kv_cache,
+                                      const int32_t* block_table,
+                                      const int32_t* query_start_loc, const int32_t* seq_lens,
+                                      float scale, int32_t causal, int32_t window, void* out,
+                                      float* lse, void* workspace, size_t workspace_bytes,
+                                      const int32_t* schedule, size_t schedule_bytes,
+                                      void* stream);
+
 /* attn_status_str: static, NUL-terminated name of a status code ("ATTN_OK", ...). */
 const char* attn_status_str(int32_t status);
 

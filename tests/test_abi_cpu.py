@@ -289,3 +289,28 @@ def test_fp8_write_argument_errors():
     assert w(_desc(), stride=260) == A.ATTN_ERR_SHAPE                # 520 bytes
     assert w(_desc(head_size=96)) == A.ATTN_ERR_UNSUPPORTED
     assert w(_desc(num_tokens=0)) == A.ATTN_OK
+
+
+# ---------------------------------------------------------------- prefill work schedule
+def test_schedule_sizes_and_errors():
+    d = _desc(max_query_len=600, max_seq_len=40)
+    with pytest.raises(A.AttnError):
+        A.attn_schedule_bytes(d)                       # max_query_len > max_seq_len
+    d = _desc(max_query_len=30, max_seq_len=40)      # 1 prefill request, 1 q tile
+    assert A.attn_schedule_bytes(d) == 256
+    big = _desc(num_seqs=300, num_tokens=5, num_decodes=0, max_query_len=1000,
+                max_seq_len=1000, max_blocks_per_seq=63)
+    assert A.attn_schedule_bytes(big) == -(-(4 * (1 + 300 * 4)) // 256) * 256
+    lib = A.lib()
+    assert lib.attn_build_schedule(ctypes.byref(d), FAKE, FAKE, 1, 0, None, 0, None) == \
+        A.ATTN_ERR_WORKSPACE
+    assert lib.attn_build_schedule(ctypes.byref(d), FAKE, FAKE, 1, 0, FAKE, 255, None) == \
+        A.ATTN_ERR_WORKSPACE
+    assert lib.attn_build_schedule(ctypes.byref(d), FAKE, FAKE, 0, 8, FAKE, 256, None) == \
+        A.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_varlen_fwd_scheduled(ctypes.byref(_desc(dtype=A.ATTN_F32)), FAKE, FAKE, FAKE,
+                                         FAKE, FAKE, 0.1, 1, 0, FAKE, None, None, 0, FAKE, 256,
+                                         None) == A.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_varlen_fwd_scheduled(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 1,
+                                         0, FAKE, None, FAKE, 1 << 20, None, 0, None) == \
+        A.ATTN_ERR_WORKSPACE

@@ -1,0 +1,111 @@
+"""The device-built prefill schedule and the scheduled forward call: the schedule holds every
+work item once with non-increasing cost (checked against the oracle's items, which are
+defined from the attention mask; equal-cost items may come in any order), and the scheduled
+call's results are bit-identical to the plain call's and match the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import exact_softmax_attention_paged_amd as A
+import gen
+import oracle
+from parity import compare, device_meta, oracle_on
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _desc(b):
+    return A.make_desc(num_seqs=b.num_seqs, num_tokens=b.num_tokens, num_decodes=b.num_decodes,
+                       max_query_len=b.max_query_len, max_seq_len=b.max_seq_len,
+                       num_heads=b.num_heads, num_kv_heads=b.num_kv_heads, head_size=b.head_size,
+                       num_blocks=b.num_blocks, block_size=b.block_size,
+                       max_blocks_per_seq=b.max_blocks_per_seq, dtype=A.ATTN_BF16)
+
+
+def build(b, causal, window):
+    desc = _desc(b)
+    bt, qsl, sl = device_meta(b, DEV)
+    sched = torch.empty(A.attn_schedule_bytes(desc) // 4, dtype=torch.int32, device=DEV)
+    A.attn_build_schedule(desc, qsl, sl, causal, window, sched)
+    return desc, sched
+
+
+BATCHES = [
+    ("varlen-causal-d64", dict(ql=[200, 1, 1000, 640, 33, 257], sl=[200, 300, 1000, 2000, 900, 257],
+                               hq=12, hkv=12, d=64, bs=16)),
+    ("mixed-d128-gqa4", dict(ql=[1, 1, 1, 700, 1500, 64], sl=[100, 3000, 5, 4000, 1500, 5000],
+                             hq=16, hkv=4, d=128, bs=32)),
+]
+
+
+def _batch(name, kw):
+    seed = 80 + [x[0] for x in BATCHES].index(name)
+    ql = kw["ql"]
+    order = np.argsort([q != 1 for q in ql], kind="stable")      # decode rows first
+    return gen.make_batch(name, num_heads=kw["hq"], num_kv_heads=kw["hkv"], head_size=kw["d"],
+                          block_size=kw["bs"], dtype="bf16", query_lens=np.array(ql)[order],
+                          seq_lens=np.array(kw["sl"])[order], passes=[(True, 0)], seed=seed,
+                          pool_factor=2), seed
+
+
+MASKS = [(False, 0), (True, 0), (True, 300)]
+
+
+@pytest.mark.parametrize("name,kw", BATCHES, ids=[x[0] for x in BATCHES])
+@pytest.mark.parametrize("causal,window", MASKS, ids=["noncausal", "causal", "w300"])
+def test_schedule_lists_every_item_longest_first(name, kw, causal, window):
+    b, _ = _batch(name, kw)
+    print(f"[case] schedule {name} causal={causal} window={window}", flush=True)
+    desc, sched = build(b, causal, window)
+    torch.cuda.synchronize()
+    s = sched.cpu().numpy()
+    items = oracle.prefill_items(b.query_lens, b.seq_lens, b.num_decodes, causal, window)
+    maxq = -(-b.max_query_len // 256)
+    cost = {(r, t): c for r, t, c in items}
+    n = int(s[0])
+    assert n == len(items)
+    listed = [(b.num_decodes + e // maxq, e % maxq) for e in s[1:1 + n]]
+    assert sorted(listed) == sorted(cost)                     # every item exactly once
+    costs = [cost[x] for x in listed]
+    assert all(a >= c for a, c in zip(costs, costs[1:])), costs   # longest first
+
+
+@pytest.mark.parametrize("name,kw", BATCHES, ids=[x[0] for x in BATCHES])
+@pytest.mark.parametrize("causal,window", MASKS, ids=["noncausal", "causal", "w300"])
+def test_scheduled_call_matches_plain_call_and_oracle(name, kw, causal, window):
+    b, seed = _batch(name, kw)
+    print(f"[case] scheduled fwd {name} causal={causal} window={window}", flush=True)
+    q, kv = gen.make_tensors(b, seed, DEV, poison=True)
+    desc, sched = build(b, causal, window)
+    bt, qsl, sl = device_meta(b, DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(A.attn_workspace_bytes(desc), 1), dtype=torch.uint8, device=DEV)
+    A.attn_varlen_fwd_scheduled(desc, q, kv, bt, qsl, sl, b.scale, causal, window, out, lse, ws,
+                                sched)
+    out2 = torch.empty_like(q)
+    lse2 = torch.empty_like(lse)
+    A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl, b.scale, causal, window, out2, lse2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    ref_out, ref_lse = oracle_on(b, q, kv, causal, window)
+    compare(out, lse, ref_out, ref_lse, label=name)
+
+
+def test_one_schedule_serves_several_layers():
+    name, kw = BATCHES[1]
+    b, seed = _batch(name, kw)
+    desc, sched = build(b, True, 0)
+    bt, qsl, sl = device_meta(b, DEV)
+    ws = torch.empty(max(A.attn_workspace_bytes(desc), 1), dtype=torch.uint8, device=DEV)
+    for layer in range(2):
+        q = gen.make_q(b, seed, DEV, layer=layer)
+        kv = gen.make_kv(b, seed, DEV, layer=layer, poison=True)
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=DEV)
+        A.attn_varlen_fwd_scheduled(desc, q, kv, bt, qsl, sl, b.scale, True, 0, out, lse, ws,
+                                    sched)
+        torch.cuda.synchronize()
+        ref_out, ref_lse = oracle_on(b, q, kv, True, 0)
+        compare(out, lse, ref_out, ref_lse, label=f"layer {layer}")
