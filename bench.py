@@ -322,16 +322,24 @@ def fp8_decode_report(dev, seed):
         keys = int(b.seq_lens.astype(np.int64).sum())
         extra = nd * (b.num_heads * b.head_size * 2 * 2 + b.num_heads * 4) + \
             int(sum(-(-int(x) // b.block_size) for x in b.seq_lens)) * 4
-        for name, elem, fn in (
-                ("bf16", 2, lambda: A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl, b.scale, True, 0,
-                                                      out, lse, ws)),
-                ("e4m3", 1, lambda: A.attn_fp8_decode_fwd(desc, q, codes, bt, qsl, sl, b.scale,
-                                                          0.0125, 0.02, 0, out, lse, ws))):
+        runs = []
+        for pt in (512, 1024, 2048):
+            d_pt = A.make_desc(num_seqs=b.num_seqs, num_tokens=b.num_tokens, num_decodes=nd,
+                               max_query_len=1, max_seq_len=b.max_seq_len,
+                               num_heads=b.num_heads, num_kv_heads=b.num_kv_heads,
+                               head_size=b.head_size, num_blocks=b.num_blocks,
+                               block_size=b.block_size, max_blocks_per_seq=b.max_blocks_per_seq,
+                               dtype=A.ATTN_BF16, partition_tokens=pt)
+            runs.append(("bf16", pt, 2, lambda d_pt=d_pt: A.attn_varlen_fwd(
+                d_pt, q, kv, bt, qsl, sl, b.scale, True, 0, out, lse, ws)))
+            runs.append(("e4m3", pt, 1, lambda d_pt=d_pt: A.attn_fp8_decode_fwd(
+                d_pt, q, codes, bt, qsl, sl, b.scale, 0.0125, 0.02, 0, out, lse, ws)))
+        for name, pt, elem, fn in runs:
             ms = _time_ms(fn, 20)
             byts = keys * 2 * b.num_kv_heads * b.head_size * elem + extra
             print(json.dumps({"report": "fp8-decode", "workload": gen.CONFIG_NAMES[k] +
                               (" (its 120 decode requests)" if k == 5 else ""), "cache": name,
-                              "ms": round(ms, 4), "bytes": byts,
+                              "partition_tokens": pt, "ms": round(ms, 4), "bytes": byts,
                               "gbps": round(byts / (ms / 1e3) / 1e9, 1),
                               "frac_of_8tbps": round(byts / (ms / 1e3) / PEAK_HBM_BYTES, 4),
                               "tokens_per_s": round(keys / (ms / 1e3), 1)}), flush=True)
