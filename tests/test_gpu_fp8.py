@@ -84,7 +84,8 @@ def test_fp8_decode_workload4_shape_sampled():
     print("[case] fp8 decode cfg4 shape", flush=True)
     codes = fp8_cache(b, 4)
     q = gen.make_q(b, 4, DEV)
-    out, lse = run_fp8_decode(b, q, torch.from_numpy(codes).to(DEV), 0)
+    out, lse = run_fp8_decode(b, q, torch.from_numpy(codes).to(DEV), 0,
+                              partition_tokens=512)       # the workload's partition length
     torch.cuda.synchronize()
     order = np.argsort(b.seq_lens)
     req = sorted(set(order[:6].tolist() + order[-6:].tolist() + [3, 100, 200]))

@@ -86,8 +86,8 @@ def test_workload_full_parity(k):
     print(compare(out, lse, ref_out, ref_lse, label=f"cfg{k}"))
 
 
-def _sampled_parity(b, q, kv, causal, window, requests, rows_per_request):
-    out, lse = run_library(b, q, kv, causal, window)
+def _sampled_parity(b, q, kv, causal, window, requests, rows_per_request, partition_tokens=0):
+    out, lse = run_library(b, q, kv, causal, window, partition_tokens=partition_tokens)
     torch.cuda.synchronize()
     sub, qs, kvs = gen.subset(b, requests, q, kv)
     qsl_sub = sub.query_start_loc
@@ -112,7 +112,8 @@ def test_workload4_sampled_parity():
     order = np.argsort(b.seq_lens)
     req = sorted(set(order[:8].tolist() + order[-8:].tolist() +
                      np.random.default_rng(0).choice(256, 32, replace=False).tolist()))
-    print(_sampled_parity(b, q, kv, True, 0, req, 1))
+    # the workload names split-KV partitions of 512 tokens
+    print(_sampled_parity(b, q, kv, True, 0, req, 1, partition_tokens=512))
 
 
 @pytest.mark.parametrize("layer", [0, 1])
