@@ -74,7 +74,8 @@ size_t round256(int64_t bytes) { return (size_t)ceil_div(bytes, 256) * 256; }
 
 // Key slices of the cascade prefix pass. Its rows are the (token, q head) pairs of each GQA
 // group, 256 per workgroup; with few rows the prefix keys are split into slices (at least 512
-// keys each, a multiple of the 64-key tile) until about 512 workgroups run.
+// keys each, a multiple of the prefill kernel's key tile: 128 keys for head_size 128, 64 for
+// 64) until about 512 workgroups run.
 struct PrefixSplit {
   int32_t slices, slice_keys;
 };
@@ -85,7 +86,8 @@ PrefixSplit prefix_split(const attn_desc* d, int32_t prefix) {
   const int64_t max_s = ceil_div(prefix, 512);
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
-  const int64_t keys = ceil_div(ceil_div(prefix, s), 64) * 64;
+  const int64_t tile = d->head_size == 128 ? 128 : 64;
+  const int64_t keys = ceil_div(ceil_div(prefix, s), tile) * tile;
   return {(int32_t)ceil_div(prefix, keys), (int32_t)keys};
 }
 

@@ -33,7 +33,8 @@ struct PrefillParams {
                                 // keys of block-table row 0 (the prefix pass, no mask). Its
                                 // rows are (token, q head) pairs of one kv head's GQA group
                                 // (grid y = kv head), and grid z splits the keys into slices
-                                // of single_slice keys (a multiple of 64), slice z writing its
+                                // of single_slice keys (a multiple of the kernel's key tile:
+                                // 128 for head_size 128, 64 for 64), slice z writing its
                                 // partial result at out_f32 / lse + z * slice_stride rows
   int32_t single_slice;
   int64_t slice_stride;         // (token, head) rows between slices of out_f32 and lse
