@@ -1,8 +1,13 @@
 """Pins of the work-item oracle (prefill items and their costs from the attention mask):
-hand-computed costs for non-causal, causal and windowed tiles, decode rows excluded."""
-import numpy as np
+hand-computed costs for non-causal, causal and windowed tiles, decode rows excluded; each
+planted mistake in a copy of the oracle fails one of them."""
+import inspect
+import types
+
+import pytest
 
 import oracle
+import oracle.schedule as osch
 
 
 def test_non_causal_tiles_read_every_key_tile():
@@ -30,3 +35,34 @@ def test_window_cuts_the_left_edge():
 def test_decode_rows_are_not_items():
     items = oracle.prefill_items([1, 1, 40], [50, 900, 40], 2, causal=True, window=0)
     assert items == [(2, 0, 1)]
+
+MUTATIONS = {
+    "cost_counted_from_key_zero": ("int(cols[-1] // tile_keys - cols[0] // tile_keys + 1)",
+                                   "int(cols[-1] // tile_keys + 1)"),
+    "last_key_tile_not_counted": ("int(cols[-1] // tile_keys - cols[0] // tile_keys + 1)",
+                                  "int(cols[-1] // tile_keys - cols[0] // tile_keys)"),
+    "decode_rows_included": ("range(num_decodes, len(seq_lens))", "range(0, len(seq_lens))"),
+    "tile_rows_overlap": ("vis[t * tile_rows:(t + 1) * tile_rows]",
+                          "vis[t * tile_rows:(t + 1) * tile_rows + 1]"),
+    "last_partial_tile_dropped": ("range(-(-ql // tile_rows))", "range(ql // tile_rows)"),
+}
+
+
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS))
+def test_a_planted_schedule_mistake_fails_some_pin(mutation, monkeypatch):
+    before, after = MUTATIONS[mutation]
+    src = inspect.getsource(osch)
+    assert before in src
+    src = src.replace("from .naive_attention import", "from oracle.naive_attention import")
+    mod = types.ModuleType("oracle_schedule_mutant")
+    exec(compile(src.replace(before, after, 1), "oracle_schedule_mutant", "exec"), mod.__dict__)
+    monkeypatch.setattr(oracle, "prefill_items", mod.prefill_items)
+    pins = [test_non_causal_tiles_read_every_key_tile, test_causal_costs_grow_with_the_tile,
+            test_window_cuts_the_left_edge, test_decode_rows_are_not_items]
+    failed = 0
+    for pin in pins:
+        try:
+            pin()
+        except Exception:
+            failed += 1
+    assert failed, f"no pin caught mutation {mutation}"
