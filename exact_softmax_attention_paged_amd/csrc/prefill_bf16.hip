@@ -9,10 +9,12 @@
 //
 // Work split: one workgroup = 8 waves of one (request, q head); each wave owns 32 query rows,
 // one 32-wide MFMA column block, so a workgroup covers 256 rows and every K/V tile brought on
-// chip serves 256 queries. KV is walked in 64-key tiles through two LDS buffers:
+// chip serves 256 queries. KV is walked in tiles (128 keys for d = 128, 64 for d = 64)
+// through two LDS buffers:
 //   * the next tile's K and V rows go from HBM straight into the other buffer
 //     (global_load_lds_dwordx4) while the current tile is consumed: no register staging and
-//     no LDS stores. The block ids of the tile after it are fetched at the same time, so the
+//     no LDS stores. One wave of each SIMD pair issues them; the other goes straight to its
+//     MFMAs. The block ids of the tile after it are fetched at the same time, so the
 //     addresses are ready when its loads are issued; one barrier per tile;
 //   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, Q^T held in
 //     registers as the B operand). On gfx950 this shape sustains about 1.6x the bf16 rate of
@@ -77,14 +79,22 @@ __device__ __forceinline__ void barrier_kv() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Transposing LDS read through a restrict pointer. Inlining a restrict parameter gives the
-// read alias-scope metadata; without it the compiler places a wait for every outstanding
-// direct load (including those filling the other buffer) before each such read.
+// Transposing LDS read (ds_read_b64_tr_b16) at an LDS byte address.
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 __device__ __attribute__((always_inline)) inline bf16x4 tr_read(
     const lds_shortx4* __restrict__ ptr) {
   return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                         const_cast<lds_shortx4*>(ptr)));
+}
+// Direct load of 16 bytes per lane from global memory into LDS at lds_base + 16 * lane
+// (global_load_lds_dwordx4, M0 = lds_base; s_nop covers the M0-write hazard). Issued as
+// inline assembly so that the compiler's wait-count model sees no outstanding LDS write:
+// with the intrinsic it waits for every LDS read (lgkmcnt(0)) before each MFMA operand use
+// instead of only for the one it needs. Completion is waited for explicitly (wait_vmem
+// before the tile barrier), and nothing else in these kernels uses M0.
+__device__ __forceinline__ void dma_b128(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_base) : "memory", "m0");
 }
 __device__ __forceinline__ const lds_shortx4* lds_at(uint32_t byte_addr) {
   return (const lds_shortx4*)(uintptr_t)byte_addr;
@@ -100,9 +110,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   constexpr int TPR = D / 8;          // lanes per row in a direct load (16 bytes each)
   constexpr int RPI = kWave / TPR;    // rows per direct-load instruction (4 or 8: divides 16)
   constexpr int NI = kBC / RPI;       // instructions per K (or V) tile
-  constexpr int IPW = NI / kWaves;    // of them issued by each wave
+  // Waves 0-3 (one of the two waves on each SIMD) issue all direct loads of a tile. A wave
+  // stalls at issue while the vector-memory queue is full; with the loads on one wave of each
+  // pair, the other one keeps the MFMA unit busy meanwhile (measured 2-3 % faster on gfx950
+  // than spreading the loads over all 8 waves).
+  constexpr int kDmaWaves = kWaves / 2;
+  constexpr int IPW = NI / kDmaWaves;   // of them issued by each such wave
   constexpr int TILEB = kBC * ROWB;   // bytes of one K (or V) tile
-  static_assert(IPW * kWaves == NI, "tile rows must split evenly over the waves");
+  static_assert(IPW * kDmaWaves == NI, "tile rows must split evenly over the waves");
 
   // [buffer][K, V] tiles, row-major [key][d] with 16-byte chunks XOR-swizzled per row; the
   // next tile lands in one buffer while the other is consumed
@@ -138,6 +153,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave index, uniform
   const int lane = tid % kWave;
+  const int dw = w % kDmaWaves;                     // direct-load slot of this wave
+  const bool dma_wave = w < kDmaWaves;
   const int h = lane / 32;            // half-wave
   const int lq = lane % 32;           // query column of this lane
 
@@ -197,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   const int l_slot = lane % TPR;                     // LDS chunk slot of this lane
   // group index of the first row of direct-load instruction u (u < IPW) of this wave in a tile
   auto group_of = [&](int tile, int u) {
-    return min((tile * kBC + (w + kWaves * u) * RPI) >> 4, last_group);
+    return min((tile * kBC + (dw + kDmaWaves * u) * RPI) >> 4, last_group);
   };
   auto block_index = [&](int grp) {
     return (uint32_t)(((uint64_t)(uint32_t)grp * p.group_recip) >> 32);
@@ -209,18 +226,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   };
   // Lane part of the source offset (elements) for tiles that lie wholly below seq_len: row
   // l_row of the instruction, d-chunk l_slot ^ swizzle(row). The swizzle depends on the row
-  // modulo 16, which is the same for every instruction of this wave (j RPI = w RPI mod 16).
+  // modulo 16, which is the same for every instruction of this wave (j RPI = dw RPI mod 16).
   const uint32_t lane_src =
-      (uint32_t)(l_row * kv_row + 8 * (l_slot ^ swizzle<D>(w * RPI + l_row)));
+      (uint32_t)(l_row * kv_row + 8 * (l_slot ^ swizzle<D>(dw * RPI + l_row)));
   const uint32_t head_off = (uint32_t)(kvh * D);
   auto issue_tile = [&](int tile_in, int buf, int32_t ids) {
+    if (!dma_wave) return;
     // the tile index is wave-uniform; saying so keeps the address arithmetic scalar
     const int tile = __builtin_amdgcn_readfirstlane(tile_in);
     unsigned char* const dst = sKV + buf * (2 * TILEB);
     const bool full = tile * kBC + kBC <= sl;        // wave-uniform
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
-      const int j = w + kWaves * u;                  // instruction index within the tile
+      const int j = dw + kDmaWaves * u;              // instruction index within the tile
       const int32_t blk = __builtin_amdgcn_readlane(ids, u);
       uint64_t off;
       if (full) {
@@ -239,12 +257,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
         off = (uint64_t)(uint32_t)blk * block_elems +
               (uint32_t)(slot * kv_row + head_off + 8 * (l_slot ^ swizzle<D>(row)));
       }
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(kcache + off),
-          (__attribute__((address_space(3))) void*)(dst + j * (RPI * ROWB)), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(vcache + off),
-          (__attribute__((address_space(3))) void*)(dst + TILEB + j * (RPI * ROWB)), 16, 0, 0);
+      const uint32_t lds_k = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(dst + j * (RPI * ROWB)));
+      dma_b128(kcache + off, lds_k);
+      dma_b128(vcache + off, lds_k + TILEB);
     }
   };
 
@@ -359,11 +375,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
           }
       }
 
-      // online softmax with a lazily moved reference max, one query column per lane pair
-      float mx = __builtin_fmaxf(sc[0][0], sc[0][1]);
+      // online softmax with a lazily moved reference max, one query column per lane pair;
+      // the row max and row sum use 8 independent partial results (short dependency
+      // chains) combined by a tree
+      float pm[8];
 #pragma unroll
-      for (int x = 2; x < 16 * kKT; x += 2)
-        mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[x / 16][x % 16]), sc[x / 16][x % 16 + 1]);
+      for (int i = 0; i < 8; ++i) pm[i] = __builtin_fmaxf(sc[0][2 * i], sc[0][2 * i + 1]);
+#pragma unroll
+      for (int x = 16; x < 16 * kKT; x += 16)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          pm[i] = __builtin_fmaxf(__builtin_fmaxf(pm[i], sc[x / 16][2 * i]), sc[x / 16][2 * i + 1]);
+      float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(pm[0], pm[1]), __builtin_fmaxf(pm[2], pm[3])),
+                                 __builtin_fmaxf(__builtin_fmaxf(pm[4], pm[5]), __builtin_fmaxf(pm[6], pm[7])));
       mx = max_xor32(mx);
       // move the reference when the tile max exceeds it by more than 2^kRescaleLog2
       // (always on a column's first visible key, where m_ref is -inf)
@@ -377,15 +401,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
         for (int dc = 0; dc < DC; ++dc) o[dc] *= alpha;
       }
       const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c_log2;
-      float lsum = 0.f;
+      float ps[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ps[i] = 0.f;
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           sc[kt][e] = fast_exp2(fmaf(sc[kt][e], c_log2, -mc));
-          lsum += sc[kt][e];
+          ps[e % 8] += sc[kt][e];
         }
-      l_run += lsum;
+      l_run += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
 
       // O^T += V^T . P^T, one MFMA per 16 keys: MFMA (kt, g) contracts keys
       // kb + 32kt + 16g + 8(j/4) + 4h + j%4 at k = 8h + j. P^T is elements 8g .. 8g+7 of
