@@ -401,6 +401,54 @@ def schedule_report(dev, seed):
                           "scheduled_tflops": round(f / (ts / 1e3) / 1e12, 1)}), flush=True)
 
 
+def configs_report(dev, seed):
+    """Every workload (the tiny fp32 case, the BERT-large-shaped encoder, the GPT-2-shaped
+    varlen prefill, the paged GQA decode, the mixed long-context batch) through one plain
+    attn_varlen_fwd call per layer pass, with the library's default decode partition. One
+    JSON line per (workload, pass): mean call time by HIP events, the algorithmic prefill
+    TFLOP/s and decode GB/s of that call, and its % of the MI355X roofline, (prefill flops /
+    MFMA peak + decode bytes / 8 TB/s) / call time, the MFMA peak being fp32 (157.3 TFLOP/s)
+    for the fp32 case and bf16 otherwise. The seed argument is unused: workload k has seed k."""
+    import torch
+    import exact_softmax_attention_paged_amd as A
+    import gen
+    del seed
+    for k in (1, 2, 3, 4, 5):
+        b = gen.config(k)
+        fp32 = b.dtype == "f32"
+        desc = A.make_desc(num_seqs=b.num_seqs, num_tokens=b.num_tokens,
+                           num_decodes=b.num_decodes, max_query_len=b.max_query_len,
+                           max_seq_len=b.max_seq_len, num_heads=b.num_heads,
+                           num_kv_heads=b.num_kv_heads, head_size=b.head_size,
+                           num_blocks=b.num_blocks, block_size=b.block_size,
+                           max_blocks_per_seq=b.max_blocks_per_seq,
+                           dtype=A.ATTN_F32 if fp32 else A.ATTN_BF16)
+        bt, qsl, sl = (torch.from_numpy(x).to(dev) for x in (b.block_table, b.query_start_loc,
+                                                             b.seq_lens))
+        ws = torch.empty(max(A.attn_workspace_bytes(desc), 1), dtype=torch.uint8, device=dev)
+        for li, (causal, window) in enumerate(b.passes):
+            q, kv = gen.make_tensors(b, k, dev, layer=li)
+            out = torch.empty_like(q)
+            lse = torch.empty(b.num_tokens, b.num_heads, dtype=torch.float32, device=dev)
+            reps = 10 if b.num_tokens > 10000 else 100
+            t = _time_ms(lambda: A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl, b.scale, causal,
+                                                   window, out, lse, ws), reps)
+            flops, dec_unique, dec_logical = algorithmic_work(b, causal, window)
+            peak = 157.3e12 if fp32 else PEAK_BF16_FLOPS
+            sec = t / 1e3
+            print(json.dumps({
+                "report": "configs", "workload": gen.CONFIG_NAMES[k], "pass": li,
+                "causal": causal, "window": window, "dtype": b.dtype, "call_ms": round(t, 4),
+                "prefill_gflop": round(flops / 1e9, 3),
+                "prefill_tflops": round(flops / sec / 1e12, 1) if flops else None,
+                "decode_gb_unique": round(dec_unique / 1e9, 4) if b.num_decodes else None,
+                "decode_gbps": round(dec_unique / sec / 1e9, 1) if b.num_decodes else None,
+                "pct_of_roofline": round(100 * (flops / peak + dec_unique / PEAK_HBM_BYTES) / sec,
+                                         2)}), flush=True)
+            del q, kv, out, lse
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -413,7 +461,8 @@ def main():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/prefill_traffic.json from two rocprofv3 --pmc runs")
     ap.add_argument("--record-command", default="", help="command line stored with the record")
-    ap.add_argument("--report", choices=["cascade", "kv-write", "fp8-decode", "schedule"],
+    ap.add_argument("--report", choices=["configs", "cascade", "kv-write", "fp8-decode",
+                                         "schedule"],
                     help="instead of the headline step, time one of the next-step paths "
                          "against the plain path and print one JSON line per batch")
     args = ap.parse_args()
@@ -436,6 +485,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.pmc_probe:
         pmc_probe(dev)
+    if args.report == "configs":
+        configs_report(dev, args.seed)
+        return
     if args.report == "cascade":
         cascade_report(dev, args.seed)
         return
