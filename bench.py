@@ -449,6 +449,54 @@ def configs_report(dev, seed):
         torch.cuda.empty_cache()
 
 
+def mixed_step(batch, layers, dev):
+    """The timed step's launch configuration: per layer pass, the decode rows (split-KV kernel
+    + LSE merge, their own descriptor) and then the prefill rows (prefill kernel, query starts
+    rebased to 0), both on torch's current stream. Returns step(ev=None) and the out / lse
+    tensors it writes (one per pass); with ev, step records ev[pass][0..2] around the calls."""
+    import torch
+    import exact_softmax_attention_paged_amd as A
+    nd = batch.num_decodes
+    tok0 = int(batch.query_start_loc[nd])
+    bt = torch.from_numpy(batch.block_table).to(dev)
+    sl = torch.from_numpy(batch.seq_lens).to(dev)
+    qsl_np = batch.query_start_loc
+    qsl_dec = torch.from_numpy(qsl_np[:nd + 1].copy()).to(dev)
+    qsl_pre = torch.from_numpy((qsl_np[nd:] - qsl_np[nd]).astype(np.int32)).to(dev)
+    bt_dec, bt_pre = bt[:nd].contiguous(), bt[nd:].contiguous()
+    sl_dec, sl_pre = sl[:nd].contiguous(), sl[nd:].contiguous()
+    common = dict(num_heads=batch.num_heads, num_kv_heads=batch.num_kv_heads,
+                  head_size=batch.head_size, num_blocks=batch.num_blocks,
+                  block_size=batch.block_size, max_blocks_per_seq=batch.max_blocks_per_seq,
+                  dtype=A.ATTN_BF16)
+    desc_dec = A.make_desc(num_seqs=nd, num_tokens=nd, num_decodes=nd, max_query_len=1,
+                           max_seq_len=int(batch.seq_lens[:nd].max()), **common)
+    desc_pre = A.make_desc(num_seqs=batch.num_seqs - nd, num_tokens=batch.num_tokens - tok0,
+                           num_decodes=0, max_query_len=int(batch.query_lens[nd:].max()),
+                           max_seq_len=int(batch.seq_lens[nd:].max()), **common)
+    ws = torch.empty(A.attn_workspace_bytes(desc_dec), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(q) for q, _ in layers]
+    lses = [torch.empty(batch.num_tokens, batch.num_heads, dtype=torch.float32, device=dev)
+            for _ in layers]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        for li, (q, kv) in enumerate(layers):
+            causal, window = batch.passes[li]
+            if ev is not None:
+                ev[li][0].record(stream)
+            A.attn_varlen_fwd(desc_dec, q[:nd], kv, bt_dec, qsl_dec, sl_dec, batch.scale,
+                              causal, window, outs[li][:nd], lses[li][:nd], ws, stream)
+            if ev is not None:
+                ev[li][1].record(stream)
+            A.attn_varlen_fwd(desc_pre, q[tok0:], kv, bt_pre, qsl_pre, sl_pre, batch.scale,
+                              causal, window, outs[li][tok0:], lses[li][tok0:], None, stream)
+            if ev is not None:
+                ev[li][2].record(stream)
+
+    return step, outs, lses
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -501,46 +549,8 @@ def main():
         schedule_report(dev, args.seed)
         return
     batch = gen.config(5, seed=args.seed)
-    nd = batch.num_decodes
-    tok0 = int(batch.query_start_loc[nd])
-
     layers = [gen.make_tensors(batch, args.seed, dev, layer=li) for li in range(len(batch.passes))]
-    bt = torch.from_numpy(batch.block_table).to(dev)
-    sl = torch.from_numpy(batch.seq_lens).to(dev)
-    qsl_np = batch.query_start_loc
-    qsl_dec = torch.from_numpy(qsl_np[:nd + 1].copy()).to(dev)
-    qsl_pre = torch.from_numpy((qsl_np[nd:] - qsl_np[nd]).astype(np.int32)).to(dev)
-    bt_dec, bt_pre = bt[:nd].contiguous(), bt[nd:].contiguous()
-    sl_dec, sl_pre = sl[:nd].contiguous(), sl[nd:].contiguous()
-    common = dict(num_heads=batch.num_heads, num_kv_heads=batch.num_kv_heads,
-                  head_size=batch.head_size, num_blocks=batch.num_blocks,
-                  block_size=batch.block_size, max_blocks_per_seq=batch.max_blocks_per_seq,
-                  dtype=A.ATTN_BF16)
-    desc_dec = A.make_desc(num_seqs=nd, num_tokens=nd, num_decodes=nd, max_query_len=1,
-                           max_seq_len=int(batch.seq_lens[:nd].max()), **common)
-    desc_pre = A.make_desc(num_seqs=batch.num_seqs - nd, num_tokens=batch.num_tokens - tok0,
-                           num_decodes=0, max_query_len=int(batch.query_lens[nd:].max()),
-                           max_seq_len=int(batch.seq_lens[nd:].max()), **common)
-    ws = torch.empty(A.attn_workspace_bytes(desc_dec), dtype=torch.uint8, device=dev)
-    outs = [torch.empty_like(q) for q, _ in layers]
-    lses = [torch.empty(batch.num_tokens, batch.num_heads, dtype=torch.float32, device=dev)
-            for _ in layers]
-    stream = torch.cuda.current_stream(dev)
-
-    def step(ev=None):
-        for li, (q, kv) in enumerate(layers):
-            causal, window = batch.passes[li]
-            if ev is not None:
-                ev[li][0].record(stream)
-            A.attn_varlen_fwd(desc_dec, q[:nd], kv, bt_dec, qsl_dec, sl_dec, batch.scale,
-                              causal, window, outs[li][:nd], lses[li][:nd], ws, stream)
-            if ev is not None:
-                ev[li][1].record(stream)
-            A.attn_varlen_fwd(desc_pre, q[tok0:], kv, bt_pre, qsl_pre, sl_pre, batch.scale,
-                              causal, window, outs[li][tok0:], lses[li][tok0:], None, stream)
-            if ev is not None:
-                ev[li][2].record(stream)
-
+    step, outs, lses = mixed_step(batch, layers, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

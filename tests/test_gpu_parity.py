@@ -89,6 +89,11 @@ def test_workload_full_parity(k):
 def _sampled_parity(b, q, kv, causal, window, requests, rows_per_request, partition_tokens=0):
     out, lse = run_library(b, q, kv, causal, window, partition_tokens=partition_tokens)
     torch.cuda.synchronize()
+    return _compare_sampled(b, q, kv, out, lse, causal, window, requests, rows_per_request)
+
+
+def _compare_sampled(b, q, kv, out, lse, causal, window, requests, rows_per_request):
+    """Oracle on the chosen requests only (first, last and evenly spaced rows of each)."""
     sub, qs, kvs = gen.subset(b, requests, q, kv)
     qsl_sub = sub.query_start_loc
     rows_sub, rows_full = [], []
@@ -105,15 +110,17 @@ def _sampled_parity(b, q, kv, causal, window, requests, rows_per_request, partit
     return compare(o, l, ref_out[rows_sub], ref_lse[rows_sub], label=b.name)
 
 
-def test_workload4_sampled_parity():
+@pytest.mark.parametrize("partition_tokens", [512, 0], ids=["part512", "default-part"])
+def test_workload4_sampled_parity(partition_tokens):
+    """The workload's stated 512-token partitions, and the library default (what the
+    per-workload report times)."""
     b = gen.config(4)
-    print("[case] cfg4 full size, sampled requests", flush=True)
+    print(f"[case] cfg4 full size, sampled requests, partition {partition_tokens}", flush=True)
     q, kv = gen.make_tensors(b, 4, DEV)
     order = np.argsort(b.seq_lens)
     req = sorted(set(order[:8].tolist() + order[-8:].tolist() +
                      np.random.default_rng(0).choice(256, 32, replace=False).tolist()))
-    # the workload names split-KV partitions of 512 tokens
-    print(_sampled_parity(b, q, kv, True, 0, req, 1, partition_tokens=512))
+    print(_sampled_parity(b, q, kv, True, 0, req, 1, partition_tokens=partition_tokens))
 
 
 @pytest.mark.parametrize("layer", [0, 1])
@@ -125,3 +132,22 @@ def test_workload5_sampled_parity(layer):
     dec = np.argsort(b.seq_lens[:120])
     req = sorted(set(dec[:4].tolist() + dec[-4:].tolist() + [17, 60, 99])) + list(range(120, 128))
     print(_sampled_parity(b, q, kv, causal, window, req, 12))
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_workload5_bench_launch_parity(layer):
+    """The timed step's own launch configuration (bench.mixed_step: the decode rows and the
+    prefill rows as two calls with their own descriptors) on sampled rows of both kinds."""
+    import dataclasses
+    import bench
+    b = gen.config(5)
+    q, kv = gen.make_tensors(b, 5, DEV, layer=layer)
+    bl = dataclasses.replace(b, passes=[b.passes[layer]])
+    causal, window = bl.passes[0]
+    print(f"[case] cfg5 layer {layer} in the bench launch configuration", flush=True)
+    step, outs, lses = bench.mixed_step(bl, [(q, kv)], torch.device(DEV))
+    step()
+    torch.cuda.synchronize()
+    dec = np.argsort(b.seq_lens[:120])
+    req = sorted(set(dec[:3].tolist() + dec[-3:].tolist() + [42])) + [120, 123, 127]
+    print(_compare_sampled(b, q, kv, outs[0], lses[0], causal, window, req, 8))
