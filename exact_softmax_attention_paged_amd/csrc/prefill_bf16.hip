@@ -125,13 +125,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
 
   const bool single = p.single_ql > 0;          // cascade prefix pass: one sequence
   const int group = p.num_heads / p.num_kv_heads;
+  // The prologue's loads are issued side by side wherever their addresses allow (each
+  // dependent scalar load would otherwise cost a full memory round trip before the first
+  // K/V tile is requested): the schedule count and item together, then the request's
+  // metadata together with the first tile's block ids.
+  // kernel arguments, all requested before the first wait (an empty asm that reads them
+  // keeps the compiler from loading each one behind its own branch)
+  asm volatile("" ::"s"(p.q), "s"(p.kv), "s"(p.block_table), "s"(p.qsl), "s"(p.seq_lens),
+               "s"(p.out), "s"(p.lse), "s"(p.v_offset), "s"(p.num_heads), "s"(p.num_kv_heads),
+               "s"(p.block_size), "s"(p.max_blocks), "s"(p.seq_begin), "s"(p.window),
+               "s"(p.scale), "s"(p.group_recip), "s"(p.kv_skip_blocks), "s"(p.single_ql),
+               "s"(p.single_sl), "s"(p.single_slice), "s"(p.slice_stride), "s"(p.out_f32),
+               "s"(p.schedule), "s"(p.max_qtiles), "s"(p.init_o), "s"(p.init_lse),
+               "s"(p.num_seqs), "s"(gridDim.x));
   int r, qt, hq_grid;
   if (p.schedule != nullptr) {
     // item slot blockIdx.x / num_heads of the schedule (sorted longest first), q head
-    // blockIdx.x % num_heads; slots past the item count have nothing to do
+    // blockIdx.x % num_heads; slots past the item count have nothing to do (the buffer
+    // holds an entry for every slot, so the item load is in bounds)
     const int slot = blockIdx.x / p.num_heads;
-    if (slot >= p.schedule[0]) return;
+    const int count = p.schedule[0];
     const int e = p.schedule[1 + slot];
+    asm volatile("" ::"s"(count), "s"(e));       // one wait for both loads
+    if (slot >= count) return;
     r = p.seq_begin + e / p.max_qtiles;
     qt = e % p.max_qtiles;
     hq_grid = blockIdx.x % p.num_heads;
@@ -140,28 +156,59 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
     qt = gridDim.x - 1 - blockIdx.x;           // longest (causal) tiles are dispatched first
     hq_grid = blockIdx.y;
   }
-  const int q_start = single ? 0 : p.qsl[r];
-  // query rows of this workgroup's sequence: its tokens, or in the prefix pass the
-  // (token, q head) pairs of one GQA group
-  const int ql = single ? p.single_ql * group : p.qsl[r + 1] - q_start;
-  if (qt * kBR >= ql) return;
-  // keys of this pass: [0, sl) after skipping kv_skip_blocks leading blocks
-  const int sl = single ? p.single_sl : p.seq_lens[r] - p.kv_skip_blocks * p.block_size;
-  const int cl = sl - ql;
-  const int kvh = single ? hq_grid : hq_grid / group;
-
+  r = __builtin_amdgcn_readfirstlane(r);            // wave-uniform
+  qt = __builtin_amdgcn_readfirstlane(qt);
+  hq_grid = __builtin_amdgcn_readfirstlane(hq_grid);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave index, uniform
   const int lane = tid % kWave;
   const int dw = w % kDmaWaves;                     // direct-load slot of this wave
   const bool dma_wave = w < kDmaWaves;
+  const int32_t* __restrict__ bt = p.block_table + (int64_t)r * p.max_blocks + p.kv_skip_blocks;
+  // Block ids of this wave's direct loads of tile 0, loaded beside the sequence metadata
+  // (they depend on the request only), so that the first tile's loads wait for one memory
+  // round trip less. They are used when the walk starts at tile 0 and tile 0 lies wholly
+  // below seq_len (the ids are then those fetch_ids(0) would load). The index is clamped to
+  // the block-table row and to the rows of this launch's requests, so the load is always in
+  // bounds, and it is unconditional so that it is issued before the metadata is waited for.
+  const int row_blocks = p.max_blocks - p.kv_skip_blocks;   // entries left in the row
+  int32_t ids0;
+  {
+    const int u = min(lane, IPW - 1);
+    const uint32_t grp = (uint32_t)(((dw + kDmaWaves * u) * RPI) >> 4);
+    const int bi = min((int)(((uint64_t)grp * p.group_recip) >> 32), row_blocks - 1);
+    const int64_t idx = min((int64_t)r * p.max_blocks + p.kv_skip_blocks + max(bi, 0),
+                            (int64_t)(p.seq_begin + p.num_seqs) * p.max_blocks - 1);
+    ids0 = p.block_table[idx];
+  }
+  // The request's metadata (in the prefix pass r is 0, so these loads are valid there too):
+  // three scalar loads and one wait for them, after the vector load above has been issued,
+  // so the two round trips overlap. (The compiler would use vector loads here, since it
+  // cannot prove that the kernel's stores leave this memory alone, and would wait for those
+  // before issuing the block-id load.) Nothing writes this memory during the kernel.
+  int qsl0, qsl1, slr;
+  asm volatile(
+      "s_load_dword %0, %3, 0x0\n\ts_load_dword %1, %3, 0x4\n\ts_load_dword %2, %4, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=s"(qsl0), "=s"(qsl1), "=s"(slr)
+      : "s"(p.qsl + r), "s"(p.seq_lens + r)
+      : "memory");
+  const int q_start = single ? 0 : qsl0;
+  // query rows of this workgroup's sequence: its tokens, or in the prefix pass the
+  // (token, q head) pairs of one GQA group
+  const int ql = single ? p.single_ql * group : qsl1 - qsl0;
+  // keys of this pass: [0, sl) after skipping kv_skip_blocks leading blocks
+  const int sl = single ? p.single_sl : slr - p.kv_skip_blocks * p.block_size;
+  if (qt * kBR >= ql) return;
+  const int cl = sl - ql;
+  const int kvh = single ? hq_grid : hq_grid / group;
+
   const int h = lane / 32;            // half-wave
   const int lq = lane % 32;           // query column of this lane
 
   const __bf16* __restrict__ q = static_cast<const __bf16*>(p.q);
   const __bf16* __restrict__ kcache = static_cast<const __bf16*>(p.kv);
   const __bf16* __restrict__ vcache = kcache + p.v_offset;
-  const int32_t* __restrict__ bt = p.block_table + (int64_t)r * p.max_blocks + p.kv_skip_blocks;
 
   // (token, q head) row of this lane's query column, as an index into [token][head] arrays
   const int wrow0 = qt * kBR + w * kRows;                // first query row of this wave
@@ -312,7 +359,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
 
   int32_t ids = 0;
   if (t_begin < t_end) {
-    issue_tile(t_begin, 0, fetch_ids(t_begin));
+    int32_t first_ids;
+    if (t_begin == 0 && kBC <= sl && row_blocks > 0) first_ids = ids0;
+    else first_ids = fetch_ids(t_begin);
+    issue_tile(t_begin, 0, first_ids);
     ids = fetch_ids(t_begin + 1);      // clamped to the last group: always a valid entry
   }
   wait_vmem();                         // Q, tile t_begin and the ids of tile t_begin + 1
