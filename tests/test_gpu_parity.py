@@ -151,3 +151,34 @@ def test_workload5_bench_launch_parity(layer):
     dec = np.argsort(b.seq_lens[:120])
     req = sorted(set(dec[:3].tolist() + dec[-3:].tolist() + [42])) + [120, 123, 127]
     print(_compare_sampled(b, q, kv, outs[0], lses[0], causal, window, req, 8))
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 8192)], ids=["causal", "w8192"])
+def test_very_long_contexts(causal, window):
+    """Contexts of 100K-131K keys, past the workloads' 32K: decode rows split into up to 64
+    partitions, and a prefill request of 300 queries walking about 940 key tiles. Block size
+    16, so a request spans up to 8192 blocks. Sampled rows of both kinds."""
+    b = _batch(77, ql=[1, 1, 300], sl=[131072, 100003, 120300], hq=8, hkv=2, d=128, bs=16,
+               pool_factor=1)
+    print(f"[case] very long contexts causal={causal} window={window}", flush=True)
+    q, kv = gen.make_tensors(b, 77, DEV, poison=True)
+    out, lse = run_library(b, q, kv, causal, window)
+    torch.cuda.synchronize()
+    rows = [0, 1, 2, 3, 150, 300, 301]
+    ref_out, ref_lse = oracle_on(b, q, kv, causal, window, rows=rows)
+    print(compare(out, lse, ref_out, ref_lse, rows=rows, label="very long contexts"))
+
+
+def test_many_tiny_decodes():
+    """5000 decode requests with 1..64 keys (single-key contexts included), GQA 4: many small
+    workgroups, partitions holding a handful of keys, and direct writes from the split
+    kernel. Every row is compared."""
+    rng = np.random.default_rng(123)
+    sl = rng.integers(1, 64, size=5000, endpoint=True)
+    sl[:3] = 1
+    b = _batch(123, ql=[1] * 5000, sl=sl.tolist(), hq=8, hkv=2, d=64, bs=16)
+    print("[case] 5000 tiny decodes", flush=True)
+    q, kv = gen.make_tensors(b, 123, DEV, poison=True)
+    out, lse = run_library(b, q, kv, True, 0)
+    ref_out, ref_lse = oracle_on(b, q, kv, True, 0)
+    print(compare(out, lse, ref_out, ref_lse, label="tiny decodes"))
