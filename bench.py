@@ -311,25 +311,24 @@ def fp8_decode_report(dev, seed):
         codes = codes.to(dev)
         bt, qsl, sl = (torch.from_numpy(x).to(dev) for x in (b.block_table, b.query_start_loc,
                                                              b.seq_lens))
-        desc = A.make_desc(num_seqs=b.num_seqs, num_tokens=b.num_tokens, num_decodes=nd,
-                           max_query_len=1, max_seq_len=b.max_seq_len, num_heads=b.num_heads,
-                           num_kv_heads=b.num_kv_heads, head_size=b.head_size,
-                           num_blocks=b.num_blocks, block_size=b.block_size,
-                           max_blocks_per_seq=b.max_blocks_per_seq, dtype=A.ATTN_BF16)
         out = torch.empty_like(q)
         lse = torch.empty(b.num_tokens, b.num_heads, dtype=torch.float32, device=dev)
-        ws = torch.empty(max(A.attn_workspace_bytes(desc), 1), dtype=torch.uint8, device=dev)
         keys = int(b.seq_lens.astype(np.int64).sum())
         extra = nd * (b.num_heads * b.head_size * 2 * 2 + b.num_heads * 4) + \
             int(sum(-(-int(x) // b.block_size) for x in b.seq_lens)) * 4
         runs = []
-        for pt in (512, 1024, 2048):
-            d_pt = A.make_desc(num_seqs=b.num_seqs, num_tokens=b.num_tokens, num_decodes=nd,
-                               max_query_len=1, max_seq_len=b.max_seq_len,
-                               num_heads=b.num_heads, num_kv_heads=b.num_kv_heads,
-                               head_size=b.head_size, num_blocks=b.num_blocks,
-                               block_size=b.block_size, max_blocks_per_seq=b.max_blocks_per_seq,
-                               dtype=A.ATTN_BF16, partition_tokens=pt)
+        descs = {pt: A.make_desc(num_seqs=b.num_seqs, num_tokens=b.num_tokens, num_decodes=nd,
+                                 max_query_len=1, max_seq_len=b.max_seq_len,
+                                 num_heads=b.num_heads, num_kv_heads=b.num_kv_heads,
+                                 head_size=b.head_size, num_blocks=b.num_blocks,
+                                 block_size=b.block_size,
+                                 max_blocks_per_seq=b.max_blocks_per_seq, dtype=A.ATTN_BF16,
+                                 partition_tokens=pt)
+                 for pt in (512, 1024, 2048)}
+        # one workspace large enough for the shortest partitions (the most partials)
+        ws = torch.empty(max(A.attn_workspace_bytes(dd) for dd in descs.values()),
+                         dtype=torch.uint8, device=dev)
+        for pt, d_pt in descs.items():
             runs.append(("bf16", pt, 2, lambda d_pt=d_pt: A.attn_varlen_fwd(
                 d_pt, q, kv, bt, qsl, sl, b.scale, True, 0, out, lse, ws)))
             runs.append(("e4m3", pt, 1, lambda d_pt=d_pt: A.attn_fp8_decode_fwd(

@@ -12,16 +12,24 @@
 
 namespace {
 
-// Split-KV partition length when the descriptor leaves it at 0, from max_seq_len (a host
-// scalar). Measured on gfx950 (bf16 and E4M3 decode, 64 q / 8 kv and 32 q / 8 kv heads):
-// contexts up to 2048 run fastest as one partition per request (no merge pass), contexts
-// up to 16K at 1024 keys, longer ones at 2048 (fewer, longer streams per workgroup and a
-// cheaper merge).
+// Split-KV partition length when the descriptor leaves it at 0: 2048 keys. Measured on gfx950
+// (bf16 and E4M3 decode, 64 q / 8 kv and 32 q / 8 kv heads, contexts up to 32K, with the
+// grid order below): contexts up to 2048 run fastest as one partition per request (no merge
+// pass), longer ones with 2048-key partitions (fewer, longer streams per workgroup and a
+// cheaper merge than 512 or 1024).
 int32_t partition_tokens(const attn_desc* d) {
   if (d->partition_tokens > 0) return d->partition_tokens;
-  if (d->max_seq_len <= 2048 || d->max_seq_len >= 16384) return 2048;
-  return 1024;
+  return 2048;
 }
+
+// Decode grid order. With few partitions per request (<= 8), dispatching every request's
+// first partitions before any second ones leaves the short last partitions of the requests
+// to the end of the grid, which shortens the kernel's tail (paged GQA decode, 256 requests
+// of 512..8192 keys: 5.28 -> 5.35 TB/s with 1024/2048-key partitions, from 5.02 / 4.57 in
+// request order). With many partitions per request the request order is faster (long
+// contexts sharing a prefix: every request's first partition reads the same blocks, which
+// then all run at once).
+bool partition_major(int64_t max_parts) { return max_parts <= 8; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -150,6 +158,7 @@ attn::DecodeParams decode_params(const attn_desc& d, const attn::PrefillParams& 
   dp.num_decodes = d.num_decodes;
   dp.part_tokens = partition_tokens(&d);
   dp.max_parts = (int32_t)max_parts;
+  dp.partition_major = partition_major(max_parts) ? 1 : 0;
   dp.window = pp.window;
   dp.scale = pp.scale;
   dp.group_recip = pp.group_recip;

@@ -61,8 +61,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   __shared__ int32_t sBlk[kMaxPartitionTokens / 16];   // block ids of this partition
 
   // grid: x = (kv head, head group) fastest, so that the workgroups reading the same tokens'
-  // rows (adjacent in every cache block) run side by side; y = partition; z = request
-  const int r = blockIdx.z;
+  // rows (adjacent in every cache block) run side by side; then partition and request, in
+  // the order the host chose (see DecodeParams::partition_major)
+  const int r = p.partition_major ? blockIdx.y : blockIdx.z;
   const int group = p.num_heads / p.num_kv_heads;
   const int head_groups = (group + 15) / 16;
   const int kvh = blockIdx.x / head_groups;
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   int first, nparts;
   decode_partitions(sl, p.window, p.part_tokens, &first, &nparts);
   nparts = min(nparts, p.max_parts);   // only reachable with seq_len > max_seq_len
-  const int pi = blockIdx.y;
+  const int pi = p.partition_major ? blockIdx.z : blockIdx.y;
   if (pi >= nparts) return;
   const int part = first + pi;
   const int p_start = part * p.part_tokens;
@@ -374,7 +375,9 @@ template <int D, bool FP8>
 hipError_t launch(const DecodeParams& p, hipStream_t stream) {
   const int group = p.num_heads / p.num_kv_heads;
   const int head_groups = (group + 15) / 16;
-  const dim3 grid(p.num_kv_heads * head_groups, p.max_parts, p.num_decodes);
+  const dim3 grid = p.partition_major
+                        ? dim3(p.num_kv_heads * head_groups, p.num_decodes, p.max_parts)
+                        : dim3(p.num_kv_heads * head_groups, p.max_parts, p.num_decodes);
   hipLaunchKernelGGL((decode_split_kernel<D, FP8>), grid, dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (p.max_parts <= 1 && p.pre_o == nullptr)) return e;

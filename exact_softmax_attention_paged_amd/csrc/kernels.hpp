@@ -65,6 +65,8 @@ struct DecodeParams {
   uint64_t group_recip;         // ceil(2^32 / (block_size / 16)), as in PrefillParams
   float v_scale;                // E4M3 cache only: V dequantisation scale (k_scale is folded
                                 // into scale by the host)
+  int32_t partition_major;      // grid order: nonzero = y request, z partition (all requests'
+                                // first partitions dispatched first); 0 = y partition, z request
   // Cascade suffix pass (zero / null for a plain call):
   int32_t kv_skip_blocks;       // as in PrefillParams
   const float* pre_o;           // non-null: a partial result over the prefix, fp32

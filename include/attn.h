@@ -81,9 +81,7 @@ typedef struct attn_desc {
   int32_t max_blocks_per_seq; /* row stride of block_table */
   int32_t dtype;              /* attn_dtype */
   int32_t partition_tokens;   /* split-KV partition length for decode rows: a multiple of
-                                 128 in [128, 4096], or 0 for the library's choice from
-                                 max_seq_len: 2048 when max_seq_len <= 2048 or >= 16384,
-                                 else 1024 */
+                                 128 in [128, 4096], or 0 for the library's choice (2048) */
 } attn_desc;
 
 /*
