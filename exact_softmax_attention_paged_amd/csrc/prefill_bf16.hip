@@ -514,17 +514,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
               floatx4{o[dc][4 * e4 + 0] * inv, o[dc][4 * e4 + 1] * inv,
                       o[dc][4 * e4 + 2] * inv, o[dc][4 * e4 + 3] * inv};
     } else {
-      __bf16* dst = static_cast<__bf16*>(p.out) + off;
+      // A lane holds d = 32 dc + 8 e4 + 4h .. +3 of its row for every 8-wide chunk e4. The two
+      // lanes of a row (l and l ^ 32, always both active) trade halves so that each ends with
+      // 8 consecutive d of one chunk (e4 = 2 pe + h) and writes them as one 16-byte store,
+      // half the store instructions of writing 4-element runs.
+      __bf16* dst = static_cast<__bf16*>(p.out) + th * D;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          bf16x4 v;
-          v[0] = to_bf16(o[dc][4 * e4 + 0] * inv);
-          v[1] = to_bf16(o[dc][4 * e4 + 1] * inv);
-          v[2] = to_bf16(o[dc][4 * e4 + 2] * inv);
-          v[3] = to_bf16(o[dc][4 * e4 + 3] * inv);
-          *reinterpret_cast<bf16x4*>(dst + 32 * dc + 8 * e4) = v;
+        for (int pe = 0; pe < 2; ++pe) {
+          floatx4 lo, hi;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a = o[dc][4 * (2 * pe) + i] * inv;        // chunk 2 pe, this lane's half
+            const float b = o[dc][4 * (2 * pe + 1) + i] * inv;    // chunk 2 pe + 1
+            const float got = __shfl_xor(h ? a : b, 32);
+            lo[i] = h ? got : a;
+            hi[i] = h ? b : got;
+          }
+          *reinterpret_cast<bf16x8*>(dst + 32 * dc + 8 * (2 * pe + h)) = pack_bf16x8(lo, hi);
         }
     }
     if (p.lse != nullptr && h == 0) {
