@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   asm volatile(
       "s_load_dword %0, %3, 0x0\n\ts_load_dword %1, %3, 0x4\n\ts_load_dword %2, %4, 0x0\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=s"(qsl0), "=s"(qsl1), "=s"(slr)
+      : "=&s"(qsl0), "=&s"(qsl1), "=&s"(slr)   // early clobber: written before the inputs are read
       : "s"(p.qsl + r), "s"(p.seq_lens + r)
       : "memory");
   const int q_start = single ? 0 : qsl0;
