@@ -65,10 +65,15 @@ def algorithmic_work(batch, causal, window):
     return prefill_flops, unique, logical
 
 
+CPU_DECODE_STEP = 2      # every 2nd decode request ...
+CPU_PREFILL_ROWS = 20    # ... and 20 query rows of each prefill request: 10-15 s of oracle
+
+
 def cpu_baseline(batch, layers, seed):
-    """Time the oracle on a bounded sample: every 10th decode request and 4 query rows of each
-    prefill request, for every layer pass; scale to the metric's unit (percent of the MI355X
-    roofline the CPU reaches on that sample)."""
+    """Time the oracle on a bounded sample: every CPU_DECODE_STEP-th decode request and
+    CPU_PREFILL_ROWS evenly spaced query rows of each prefill request, for every layer pass;
+    scale to the metric's unit (percent of the MI355X roofline the CPU reaches on that
+    sample)."""
     import torch
     import gen
     import oracle
@@ -78,7 +83,7 @@ def cpu_baseline(batch, layers, seed):
     except Exception:
         threads = os.cpu_count() or 1
     nd = batch.num_decodes
-    dec = list(range(0, nd, 10))
+    dec = list(range(0, nd, CPU_DECODE_STEP))
     pre = list(range(nd, batch.num_seqs))
     floor_s = 0.0
     cpu_s = 0.0
@@ -89,7 +94,7 @@ def cpu_baseline(batch, layers, seed):
         rows = list(range(len(dec)))
         for i in range(len(dec), sub.num_seqs):
             ql = int(sub.query_lens[i])
-            rows += [int(qsl[i]) + x for x in np.linspace(0, ql - 1, 4).astype(int)]
+            rows += [int(qsl[i]) + x for x in np.linspace(0, ql - 1, CPU_PREFILL_ROWS).astype(int)]
         qn = qs.to(torch.float32).numpy()
         kvn = kvs.to(torch.float32).numpy()
         t0 = time.perf_counter()
@@ -101,7 +106,7 @@ def cpu_baseline(batch, layers, seed):
         flops = 0.0
         for i in range(len(dec), sub.num_seqs):
             ql, sl = int(sub.query_lens[i]), int(sub.seq_lens[i])
-            pos = (sl - ql) + np.linspace(0, ql - 1, 4).astype(int)
+            pos = (sl - ql) + np.linspace(0, ql - 1, CPU_PREFILL_ROWS).astype(int)
             lo = np.maximum(pos - window + 1, 0) if window > 0 else 0
             flops += 4.0 * d * hq * float(np.sum(pos + 1 - lo))
         byts = 0.0
@@ -113,9 +118,10 @@ def cpu_baseline(batch, layers, seed):
     return {"value": 100.0 * floor_s / cpu_s, "unit": "% of MI355X roofline", "cores": threads,
             "kind": "oracle", "seconds": round(cpu_s, 3),
             "sample": f"fp64 numpy oracle; per layer pass: decode requests {dec[0]}..{dec[-1]} "
-                      f"step 10 ({len(dec)} of {nd}) and 4 evenly spaced query rows of each of "
-                      f"the {len(pre)} prefill requests, all 64 q heads; value = GPU-roofline "
-                      f"time of that work / CPU time"}
+                      f"step {CPU_DECODE_STEP} ({len(dec)} of {nd}) and {CPU_PREFILL_ROWS} evenly "
+                      f"spaced query rows of each of the {len(pre)} prefill requests, all "
+                      f"{batch.num_heads} q heads; value = GPU-roofline time of that work / CPU "
+                      f"time"}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
