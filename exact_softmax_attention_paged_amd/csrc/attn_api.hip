@@ -54,6 +54,8 @@ attn_status check_desc(const attn_desc* d) {
   if ((int64_t)d->max_seq_len * d->block_size >= ((int64_t)1 << 40)) return ATTN_ERR_SHAPE;
   if ((int64_t)d->block_size * d->num_kv_heads * d->head_size >= ((int64_t)1 << 31))
     return ATTN_ERR_SHAPE;                                            // one block < 2^31 elements
+  // decode partitions per request: a grid dimension (y or z) of the split kernel
+  if (ceil_div(d->max_seq_len, partition_tokens(d)) > 65535) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
 

@@ -130,8 +130,9 @@ attn_status attn_workspace_bytes(const attn_desc* desc, size_t* bytes);
  *   stream          hipStream_t to queue on (NULL = the null stream). The call returns as
  *                   soon as the kernels are queued.
  *
- * Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_BLOCK_SIZE ([FA] Backend raises on
- * block_size % 16 != 0), ATTN_ERR_GQA, ATTN_ERR_UNSUPPORTED (head_size not 64/128, unknown
+ * Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE (negative or inconsistent sizes, more than 65535
+ * requests or than 65535 decode partitions of max_seq_len), ATTN_ERR_BLOCK_SIZE ([FA] Backend
+ * raises on block_size % 16 != 0), ATTN_ERR_GQA, ATTN_ERR_UNSUPPORTED (head_size not 64/128, unknown
  * dtype, partition_tokens not a multiple of 128 in [128, 4096], window > 0 without
  * causal, scale not finite and > 0),
  * ATTN_ERR_WORKSPACE, ATTN_ERR_HIP (launch failure).

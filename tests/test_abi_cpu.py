@@ -66,6 +66,9 @@ def _fwd(desc, causal=1, window=0, scale=0.125, ws=None, ws_bytes=0, q=FAKE, out
     (dict(num_tokens=-1), A.ATTN_ERR_SHAPE),
     (dict(max_seq_len=49), A.ATTN_ERR_SHAPE),       # exceeds max_blocks_per_seq * block_size
     (dict(max_query_len=41), A.ATTN_ERR_SHAPE),
+    # more than 65535 decode partitions of max_seq_len (a grid dimension of the split kernel)
+    (dict(partition_tokens=128, max_seq_len=128 * 65535 + 1,
+          max_blocks_per_seq=(128 * 65535) // 16 + 1), A.ATTN_ERR_SHAPE),
 ])
 def test_descriptor_errors(kw, status):
     d = _desc(**kw)
@@ -91,7 +94,7 @@ def test_null_pointers():
 def test_workspace_size_and_check():
     d = _desc(num_decodes=1, max_seq_len=40)
     need = A.attn_workspace_bytes(d)
-    parts = -(-40 // 512)
+    parts = -(-40 // 2048)                     # the default partition length
     assert need == -(-(1 * 8 * parts * 129 * 4) // 256) * 256
     assert _fwd(d, ws=None, ws_bytes=0) == A.ATTN_ERR_WORKSPACE
     assert _fwd(d, ws=FAKE, ws_bytes=need - 1) == A.ATTN_ERR_WORKSPACE
