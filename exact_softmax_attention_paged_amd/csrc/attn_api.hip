@@ -13,23 +13,14 @@
 namespace {
 
 // Split-KV partition length when the descriptor leaves it at 0: 2048 keys. Measured on gfx950
-// (bf16 and E4M3 decode, 64 q / 8 kv and 32 q / 8 kv heads, contexts up to 32K, with the
-// grid order below): contexts up to 2048 run fastest as one partition per request (no merge
-// pass), longer ones with 2048-key partitions (fewer, longer streams per workgroup and a
-// cheaper merge than 512 or 1024).
+// (bf16 and E4M3 decode, 64 q / 8 kv and 32 q / 8 kv heads, contexts up to 32K): contexts up
+// to 2048 run fastest as one partition per request (no merge pass), longer ones with
+// 2048-key partitions (fewer, longer streams per workgroup and a cheaper merge than 512 or
+// 1024).
 int32_t partition_tokens(const attn_desc* d) {
   if (d->partition_tokens > 0) return d->partition_tokens;
   return 2048;
 }
-
-// Decode grid order. With few partitions per request (<= 8), dispatching every request's
-// first partitions before any second ones leaves the short last partitions of the requests
-// to the end of the grid, which shortens the kernel's tail (paged GQA decode, 256 requests
-// of 512..8192 keys: 5.28 -> 5.35 TB/s with 1024/2048-key partitions, from 5.02 / 4.57 in
-// request order). With many partitions per request the request order is faster (long
-// contexts sharing a prefix: every request's first partition reads the same blocks, which
-// then all run at once).
-bool partition_major(int64_t max_parts) { return max_parts <= 8; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -54,8 +45,12 @@ attn_status check_desc(const attn_desc* d) {
   if ((int64_t)d->max_seq_len * d->block_size >= ((int64_t)1 << 40)) return ATTN_ERR_SHAPE;
   if ((int64_t)d->block_size * d->num_kv_heads * d->head_size >= ((int64_t)1 << 31))
     return ATTN_ERR_SHAPE;                                            // one block < 2^31 elements
-  // decode partitions per request: a grid dimension (y or z) of the split kernel
+  // decode partitions per request, and the split kernel's 1-D grid of (request, partition,
+  // kv head, head group) workgroups
   if (ceil_div(d->max_seq_len, partition_tokens(d)) > 65535) return ATTN_ERR_SHAPE;
+  if ((int64_t)d->num_decodes * ceil_div(d->max_seq_len, partition_tokens(d)) * d->num_kv_heads *
+          ceil_div(d->num_heads / d->num_kv_heads, 16) >= ((int64_t)1 << 31))
+    return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
 
@@ -73,11 +68,17 @@ int64_t decode_max_parts(const attn_desc* d, int32_t window) {
   return n < 1 ? 1 : n;
 }
 
+// Split-KV workspace: the partitions' fp32 results ([num_decodes][Hq][max_parts][d], then
+// [num_decodes][Hq][max_parts] log-sum-exps), then, from a 256-byte boundary, the decode work
+// schedule (one count and one int32 per (request, partition) slot).
+int64_t decode_results_bytes(const attn_desc* d, int64_t max_parts) {
+  const int64_t rows = (int64_t)d->num_decodes * d->num_heads * max_parts;
+  return ceil_div((rows * d->head_size + rows) * 4, 256) * 256;
+}
 size_t workspace_for(const attn_desc* d, int64_t max_parts) {
   if (!uses_split_decode(d)) return 0;
-  const int64_t rows = (int64_t)d->num_decodes * d->num_heads * max_parts;
-  const int64_t floats = rows * d->head_size + rows;
-  return (size_t)ceil_div(floats * 4, 256) * 256;
+  const int64_t sched = (1 + (int64_t)d->num_decodes * max_parts) * 4;
+  return (size_t)(decode_results_bytes(d, max_parts) + ceil_div(sched, 256) * 256);
 }
 
 size_t round256(int64_t bytes) { return (size_t)ceil_div(bytes, 256) * 256; }
@@ -160,7 +161,8 @@ attn::DecodeParams decode_params(const attn_desc& d, const attn::PrefillParams& 
   dp.num_decodes = d.num_decodes;
   dp.part_tokens = partition_tokens(&d);
   dp.max_parts = (int32_t)max_parts;
-  dp.partition_major = partition_major(max_parts) ? 1 : 0;
+  dp.schedule = reinterpret_cast<const int32_t*>(reinterpret_cast<char*>(ws) +
+                                                 decode_results_bytes(&d, max_parts));
   dp.window = pp.window;
   dp.scale = pp.scale;
   dp.group_recip = pp.group_recip;

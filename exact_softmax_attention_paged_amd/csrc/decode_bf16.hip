@@ -60,13 +60,19 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   __shared__ float sL[kWaves][16];
   __shared__ int32_t sBlk[kMaxPartitionTokens / 16];   // block ids of this partition
 
-  // grid: x = (kv head, head group) fastest, so that the workgroups reading the same tokens'
-  // rows (adjacent in every cache block) run side by side; then partition and request, in
-  // the order the host chose (see DecodeParams::partition_major)
-  const int r = p.partition_major ? blockIdx.y : blockIdx.z;
+  // grid x = item slot * heads_wg + (kv head, head group): the workgroups of one item read
+  // the same tokens' rows (adjacent in every cache block) side by side, and the items come
+  // from the decode schedule, longest partition first
   const int group = p.num_heads / p.num_kv_heads;
   const int head_groups = (group + 15) / 16;
-  const int kvh = blockIdx.x / head_groups;
+  const int heads_wg = p.num_kv_heads * head_groups;
+  const int slot = blockIdx.x / heads_wg;
+  const int count = p.schedule[0];
+  const int item = p.schedule[1 + min(slot, p.num_decodes * p.max_parts - 1)];
+  if (slot >= count) return;
+  const int r = item / p.max_parts;
+  const int pi = item % p.max_parts;
+  const int kvh = (blockIdx.x % heads_wg) / head_groups;
   const int hg = blockIdx.x % head_groups;
   const int nh = min(16, group - hg * 16);             // q heads in this workgroup
   const int h0 = kvh * group + hg * 16;                // first q head
@@ -76,8 +82,6 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   int first, nparts;
   decode_partitions(sl, p.window, p.part_tokens, &first, &nparts);
   nparts = min(nparts, p.max_parts);   // only reachable with seq_len > max_seq_len
-  const int pi = p.partition_major ? blockIdx.z : blockIdx.y;
-  if (pi >= nparts) return;
   const int part = first + pi;
   const int p_start = part * p.part_tokens;
   const int lo = p.window > 0 ? max(0, sl - p.window) : 0;
@@ -371,15 +375,25 @@ __global__ __launch_bounds__(64) void lse_merge_kernel(const DecodeParams p) {
   if (p.lse != nullptr && lane == 0) p.lse[row] = L;
 }
 
+// The schedule kernel, then one workgroup per (schedule slot, kv head, head group) (slots past
+// the item count exit at once), then the merge. The schedule lives in the caller's workspace.
 template <int D, bool FP8>
 hipError_t launch(const DecodeParams& p, hipStream_t stream) {
   const int group = p.num_heads / p.num_kv_heads;
   const int head_groups = (group + 15) / 16;
-  const dim3 grid = p.partition_major
-                        ? dim3(p.num_kv_heads * head_groups, p.num_decodes, p.max_parts)
-                        : dim3(p.num_kv_heads * head_groups, p.max_parts, p.num_decodes);
+  DecodeScheduleParams sp{};
+  sp.seq_lens = p.seq_lens;
+  sp.schedule = const_cast<int32_t*>(p.schedule);
+  sp.num_decodes = p.num_decodes;
+  sp.part_tokens = p.part_tokens;
+  sp.max_parts = p.max_parts;
+  sp.window = p.window;
+  sp.kv_skip_keys = p.kv_skip_blocks * p.block_size;
+  hipError_t e = launch_decode_schedule(sp, stream);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((int64_t)p.num_decodes * p.max_parts * p.num_kv_heads * head_groups));
   hipLaunchKernelGGL((decode_split_kernel<D, FP8>), grid, dim3(256), 0, stream, p);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess || (p.max_parts <= 1 && p.pre_o == nullptr)) return e;
   hipLaunchKernelGGL(lse_merge_kernel<D>, dim3(p.num_heads, p.num_decodes), dim3(kWave), 0,
                      stream, p);

@@ -65,8 +65,8 @@ struct DecodeParams {
   uint64_t group_recip;         // ceil(2^32 / (block_size / 16)), as in PrefillParams
   float v_scale;                // E4M3 cache only: V dequantisation scale (k_scale is folded
                                 // into scale by the host)
-  int32_t partition_major;      // grid order: nonzero = y request, z partition (all requests'
-                                // first partitions dispatched first); 0 = y partition, z request
+  const int32_t* schedule;      // work items, longest first (see DecodeScheduleParams): grid
+                                // x = item slot * (num_kv_heads * head groups) + kv head group
   // Cascade suffix pass (zero / null for a plain call):
   int32_t kv_skip_blocks;       // as in PrefillParams
   const float* pre_o;           // non-null: a partial result over the prefix, fp32
@@ -122,7 +122,19 @@ struct ScheduleParams {
   int32_t causal, window;
 };
 
+// Decode work schedule: items (decode request r, partition pi) coded r * max_parts + pi, for
+// every partition holding visible keys, sorted by their number of keys (in 16-key units),
+// longest first, so the in-order workgroup dispatch leaves the short partitions to the end of
+// the grid. schedule[0] = item count, schedule[1 + i] = item i.
+struct DecodeScheduleParams {
+  const int32_t* seq_lens;
+  int32_t* schedule;
+  int32_t num_decodes, part_tokens, max_parts, window;
+  int32_t kv_skip_keys;         // keys before the pass's range (cascade suffix pass)
+};
+
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_decode_schedule(const DecodeScheduleParams& p, hipStream_t stream);
 hipError_t launch_prefill_schedule(const ScheduleParams& p, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t stream);
 // E4M3 cache from bf16 rows: row_chunks counts 16-code chunks (slot_bytes = codes per row)

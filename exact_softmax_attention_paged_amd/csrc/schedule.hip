@@ -11,6 +11,10 @@
 //
 // Schedule buffer (int32): [0] = number of items n, [1 + i] = item i (i < n) as
 // request_offset * max_qtiles + q_tile, request_offset counting from the first prefill request.
+//
+// The split-KV decode kernel gets the same treatment on every call: its items are (decode
+// request, partition) pairs, sorted by their number of keys, so that the partial last
+// partitions of the requests run at the end of the grid instead of being spread over it.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -36,15 +40,17 @@ __device__ __forceinline__ int item_cost(const ScheduleParams& p, int e) {
   return max(tiles, 0);
 }
 
-__global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(const ScheduleParams p) {
+// Counting sort of the items [0, n_all) by cost, longest first, into schedule (one workgroup
+// of kSchedThreads threads); cost(e) < 0 drops item e. Items of equal cost keep no fixed order.
+template <class Cost>
+__device__ void sort_items(int n_all, Cost cost, int32_t* schedule) {
   __shared__ int hist[kBuckets];
   const int tid = threadIdx.x;
-  const int n_all = p.num_seqs * p.max_qtiles;
   for (int b = tid; b < kBuckets; b += kSchedThreads) hist[b] = 0;
   __syncthreads();
   // 1. histogram of the costs (bucket kBuckets - 1 - cost, so that bucket order is longest first)
   for (int e = tid; e < n_all; e += kSchedThreads) {
-    const int c = item_cost(p, e);
+    const int c = cost(e);
     if (c >= 0) atomicAdd(&hist[kBuckets - 1 - min(c, kBuckets - 1)], 1);
   }
   __syncthreads();
@@ -74,15 +80,45 @@ __global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(const S
   __syncthreads();
   // 3. scatter the items to their sorted positions
   for (int e = tid; e < n_all; e += kSchedThreads) {
-    const int c = item_cost(p, e);
+    const int c = cost(e);
     if (c < 0) continue;
     const int pos = atomicAdd(&hist[kBuckets - 1 - min(c, kBuckets - 1)], 1);
-    p.schedule[1 + pos] = e;
+    schedule[1 + pos] = e;
   }
-  if (tid == 0) p.schedule[0] = total;
+  if (tid == 0) schedule[0] = total;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(const ScheduleParams p) {
+  sort_items(p.num_seqs * p.max_qtiles, [&](int e) { return item_cost(p, e); }, p.schedule);
+}
+
+// Keys of partition pi of decode request r (the partition split of the decode kernel), in
+// 16-key units; -1 past the request's last partition.
+__device__ __forceinline__ int decode_item_cost(const DecodeScheduleParams& p, int e) {
+  const int r = e / p.max_parts;
+  const int pi = e % p.max_parts;
+  const int sl = p.seq_lens[r] - p.kv_skip_keys;
+  int first, nparts;
+  decode_partitions(sl, p.window, p.part_tokens, &first, &nparts);
+  if (pi >= min(nparts, p.max_parts)) return -1;
+  const int lo = p.window > 0 ? max(0, sl - p.window) : 0;
+  const int part = first + pi;
+  const int keys = min(sl, (part + 1) * p.part_tokens) - max(lo, part * p.part_tokens);
+  return (keys + 15) / 16;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(
+    const DecodeScheduleParams p) {
+  sort_items(p.num_decodes * p.max_parts, [&](int e) { return decode_item_cost(p, e); },
+             p.schedule);
 }
 
 }  // namespace
+
+hipError_t launch_decode_schedule(const DecodeScheduleParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_schedule(const ScheduleParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(prefill_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, p);

@@ -9,8 +9,8 @@ from .naive_attention import (attention, attend_rows, gather_kv, visible_keys,
 from .cascade import cascade_attention, merge_partials
 from .kv_write import kv_cache_write
 from .fp8 import attention_fp8_kv, e4m3_quantize, e4m3_value
-from .schedule import prefill_items
+from .schedule import decode_items, prefill_items
 
 __all__ = ["attention", "attend_rows", "gather_kv", "visible_keys", "softmax_weights",
            "flops_visible_pairs", "cascade_attention", "merge_partials", "kv_cache_write",
-           "attention_fp8_kv", "e4m3_quantize", "e4m3_value", "prefill_items"]
+           "attention_fp8_kv", "e4m3_quantize", "e4m3_value", "prefill_items", "decode_items"]

@@ -95,14 +95,17 @@ def test_workspace_size_and_check():
     d = _desc(num_decodes=1, max_seq_len=40)
     need = A.attn_workspace_bytes(d)
     parts = -(-40 // 2048)                     # the default partition length
-    assert need == -(-(1 * 8 * parts * 129 * 4) // 256) * 256
+
+    def expected(decodes, parts):              # partition results, then the work schedule
+        return (-(-(decodes * 8 * parts * 129 * 4) // 256) * 256 +
+                -(-((1 + decodes * parts) * 4) // 256) * 256)
+    assert need == expected(1, parts)
     assert _fwd(d, ws=None, ws_bytes=0) == A.ATTN_ERR_WORKSPACE
     assert _fwd(d, ws=FAKE, ws_bytes=need - 1) == A.ATTN_ERR_WORKSPACE
     big = _desc(num_decodes=1, max_seq_len=40000, max_blocks_per_seq=2500)
     parts = -(-40000 // 256)
     assert A.attn_workspace_bytes(_desc(num_decodes=1, max_seq_len=40000, max_blocks_per_seq=2500,
-                                        partition_tokens=256)) == \
-        -(-(8 * parts * 129 * 4) // 256) * 256
+                                        partition_tokens=256)) == expected(1, parts)
     assert A.attn_workspace_bytes(_desc(num_decodes=0)) == 0
     assert A.attn_workspace_bytes(_desc(dtype=A.ATTN_F32)) == 0
     assert big is not None

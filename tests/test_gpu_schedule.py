@@ -109,3 +109,49 @@ def test_one_schedule_serves_several_layers():
         torch.cuda.synchronize()
         ref_out, ref_lse = oracle_on(b, q, kv, True, 0)
         compare(out, lse, ref_out, ref_lse, label=f"layer {layer}")
+
+
+# ---- decode work schedule (built by every split-KV decode call, in the call's workspace)
+DECODE_LENS = [1, 15, 16, 17, 511, 512, 513, 2047, 2048, 2049, 4095, 4096, 4097, 6000, 9000,
+               300, 7777, 12345]
+
+
+@pytest.mark.parametrize("window,part", [(0, 0), (0, 512), (3000, 0), (100, 1024)],
+                         ids=["default", "p512", "w3000", "w100-p1024"])
+def test_decode_schedule_lists_every_partition_longest_first(window, part):
+    nd = len(DECODE_LENS)
+    print(f"[case] decode schedule window={window} partition={part}", flush=True)
+    b = gen.make_batch("decode-schedule", num_heads=8, num_kv_heads=2, head_size=64,
+                       block_size=16, dtype="bf16", query_lens=[1] * nd, seq_lens=DECODE_LENS,
+                       passes=[(True, window)], seed=91)
+    q, kv = gen.make_tensors(b, 91, DEV, poison=True)
+    desc = A.make_desc(num_seqs=nd, num_tokens=nd, num_decodes=nd, max_query_len=1,
+                       max_seq_len=b.max_seq_len, num_heads=8, num_kv_heads=2, head_size=64,
+                       num_blocks=b.num_blocks, block_size=16,
+                       max_blocks_per_seq=b.max_blocks_per_seq, dtype=A.ATTN_BF16,
+                       partition_tokens=part)
+    bt, qsl, sl = device_meta(b, DEV)
+    ws = torch.zeros(A.attn_workspace_bytes(desc), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty(nd, 8, dtype=torch.float32, device=DEV)
+    A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl, b.scale, True, window, out, lse, ws)
+    torch.cuda.synchronize()
+    # workspace layout of the C layer: partition results ([nd][Hq][max_parts][d] and
+    # [nd][Hq][max_parts] fp32, padded to 256 bytes), then the schedule
+    P = part or 2048
+    max_parts = -(-b.max_seq_len // P)
+    if window > 0:
+        max_parts = min(max_parts, -(-window // P) + 1)
+    rows = nd * 8 * max_parts
+    off = -(-(rows * 64 + rows) * 4 // 256) * 256
+    s = ws[off:off + 4 * (1 + nd * max_parts)].view(torch.int32).cpu().numpy()
+    items = oracle.decode_items(b.seq_lens, nd, window, P)
+    cost = {(r, p): c for r, p, c in items}
+    n = int(s[0])
+    assert n == len(items)
+    listed = [(int(e) // max_parts, int(e) % max_parts) for e in s[1:1 + n]]
+    assert sorted(listed) == sorted(cost)                     # every partition exactly once
+    costs = [cost[x] for x in listed]
+    assert all(a >= c for a, c in zip(costs, costs[1:])), costs   # longest first
+    ref_out, ref_lse = oracle_on(b, q, kv, True, window)
+    compare(out, lse, ref_out, ref_lse, label=f"decode schedule w{window} p{part}")

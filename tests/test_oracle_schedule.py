@@ -66,3 +66,57 @@ def test_a_planted_schedule_mistake_fails_some_pin(mutation, monkeypatch):
         except Exception:
             failed += 1
     assert failed, f"no pin caught mutation {mutation}"
+
+
+# ---- decode items: partitions of P keys of the one query row's visible keys
+def test_decode_partitions_without_window():
+    # keys 0..4999 in 2048-key partitions: 2048, 2048 and 904 keys (57 units of 16, rounded up)
+    assert oracle.decode_items([5000], 1, 0, 2048) == [(0, 0, 128), (0, 1, 128), (0, 2, 57)]
+    assert oracle.decode_items([4096], 1, 0, 2048) == [(0, 0, 128), (0, 1, 128)]
+    assert oracle.decode_items([1, 17], 2, 0, 2048) == [(0, 0, 1), (1, 0, 2)]
+
+
+def test_decode_window_starts_at_the_first_visible_partition():
+    # the row at position 4999 with W = 4096 sees keys [904, 4999]: partition 0 holds 1144 of
+    # them (72 units), then 2048 and 904
+    assert oracle.decode_items([5000], 1, 4096, 2048) == [(0, 0, 72), (0, 1, 128), (0, 2, 57)]
+    # W = 100: keys [4900, 4999], all in partition 2, numbered 0 here
+    assert oracle.decode_items([5000], 1, 100, 2048) == [(0, 0, 7)]
+
+
+def test_decode_items_skip_the_prefix_and_prefill_rows():
+    # a pass over the keys after a 2048-key prefix: 2952 keys -> 2048 + 904
+    assert oracle.decode_items([5000], 1, 0, 2048, kv_skip=2048) == [(0, 0, 128), (0, 1, 57)]
+    assert oracle.decode_items([2048], 1, 0, 2048, kv_skip=2048) == []
+    assert oracle.decode_items([30, 900], 1, 0, 512) == [(0, 0, 2)]     # row 1 is prefill
+
+
+DECODE_MUTATIONS = {
+    "partitions_numbered_from_key_zero": ("int(p) - first", "int(p)"),
+    "cost_rounded_down": ("int(-(-np.count_nonzero(parts == p) // 16))",
+                          "int(np.count_nonzero(parts == p) // 16)"),
+    "window_ignored": ("visible_keys(1, sl, True, window)", "visible_keys(1, sl, True, 0)"),
+    "prefix_not_skipped": ("int(seq_lens[r]) - kv_skip", "int(seq_lens[r])"),
+    "prefill_rows_included": ("for r in range(num_decodes):", "for r in range(len(seq_lens)):"),
+}
+
+
+@pytest.mark.parametrize("mutation", sorted(DECODE_MUTATIONS))
+def test_a_planted_decode_schedule_mistake_fails_some_pin(mutation, monkeypatch):
+    before, after = DECODE_MUTATIONS[mutation]
+    src = inspect.getsource(osch)
+    assert before in src
+    src = src.replace("from .naive_attention import", "from oracle.naive_attention import")
+    mod = types.ModuleType("oracle_schedule_mutant")
+    exec(compile(src.replace(before, after, 1), "oracle_schedule_mutant", "exec"), mod.__dict__)
+    monkeypatch.setattr(oracle, "decode_items", mod.decode_items)
+    pins = [test_decode_partitions_without_window,
+            test_decode_window_starts_at_the_first_visible_partition,
+            test_decode_items_skip_the_prefix_and_prefill_rows]
+    failed = 0
+    for pin in pins:
+        try:
+            pin()
+        except Exception:
+            failed += 1
+    assert failed, f"no pin caught mutation {mutation}"
