@@ -12,17 +12,25 @@
 
 namespace {
 
-// Split-KV partition length when the descriptor leaves it at 0: 2048 keys. Measured on gfx950
-// (bf16 and E4M3 decode, 64 q / 8 kv and 32 q / 8 kv heads, contexts up to 32K): contexts up
-// to 2048 run fastest as one partition per request (no merge pass), longer ones with
-// 2048-key partitions (fewer, longer streams per workgroup and a cheaper merge than 512 or
-// 1024).
+// Split-KV partition length when the descriptor leaves it at 0: the longest of 16384, 8192,
+// ..., 256 keys that still gives the split kernel at least 2048 workgroups (counted from
+// max_seq_len, i.e. an upper bound), else 256. With the longest-first decode schedule, longer
+// partitions measured faster on gfx950 as long as the grid keeps about four workgroups per
+// CU slot (two per CU): fewer workgroup prologues and partial results, and no merge pass for
+// requests that fit one partition (paged GQA decode, 256 requests of 512..8192 keys, 32 q / 8
+// kv heads: 0.843 / 0.836 / 0.821 ms with 2048 / 4096 / 8192 keys; 120 requests of 4K..32K
+// keys, 64 q / 8 kv heads: 1.537 / 1.523 / 1.503 ms with 2048 / 4096 / 8192 and 1.516 ms
+// with 16384, where the grid drops to 1920 workgroups).
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 int32_t partition_tokens(const attn_desc* d) {
   if (d->partition_tokens > 0) return d->partition_tokens;
-  return 2048;
+  const int64_t per_part = (int64_t)d->num_decodes * d->num_kv_heads *
+                           ceil_div(d->num_heads / d->num_kv_heads, 16);
+  for (int32_t P = attn::kMaxPartitionTokens; P > 256; P /= 2)
+    if (per_part * ceil_div(d->max_seq_len, P) >= 2048) return P;
+  return 256;
 }
-
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Checks that need nothing but the descriptor.
 attn_status check_desc(const attn_desc* d) {

@@ -7,7 +7,7 @@ namespace attn {
 
 // Largest split-KV partition the decode kernel accepts (its block-id table holds
 // kMaxPartitionTokens / 16 entries).
-constexpr int32_t kMaxPartitionTokens = 4096;
+constexpr int32_t kMaxPartitionTokens = 16384;
 
 // One prefill launch covers requests [seq_begin, seq_begin + num_seqs) and every q head.
 struct PrefillParams {

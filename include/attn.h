@@ -81,7 +81,10 @@ typedef struct attn_desc {
   int32_t max_blocks_per_seq; /* row stride of block_table */
   int32_t dtype;              /* attn_dtype */
   int32_t partition_tokens;   /* split-KV partition length for decode rows: a multiple of
-                                 128 in [128, 4096], or 0 for the library's choice (2048) */
+                                 128 in [128, 16384], or 0 for the library's choice (the
+                                 longest of 16384, 8192, ..., 256 that still yields 2048
+                                 split workgroups for num_decodes requests of max_seq_len
+                                 keys, else 256) */
 } attn_desc;
 
 /*
@@ -90,7 +93,9 @@ typedef struct attn_desc {
  * ([RBLN] Overview: partition results combined by online softmax):
  *   num_decodes * num_heads * P * (head_size + 1) * 4 bytes, rounded up to 256,
  * where P is the number of partitions of max_seq_len (capped for a window in
- * attn_varlen_fwd). Returns 0 bytes when num_decodes == 0 or dtype is ATTN_F32.
+ * attn_varlen_fwd), followed by the decode work schedule the call builds there:
+ *   (1 + num_decodes * P) * 4 bytes, rounded up to 256.
+ * Returns 0 bytes when num_decodes == 0 or dtype is ATTN_F32.
  * Errors: ATTN_ERR_NULL (desc or bytes NULL), and the same shape checks as attn_varlen_fwd
  * that do not depend on the window.
  */
@@ -133,7 +138,7 @@ attn_status attn_workspace_bytes(const attn_desc* desc, size_t* bytes);
  * Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE (negative or inconsistent sizes, more than 65535
  * requests or than 65535 decode partitions of max_seq_len), ATTN_ERR_BLOCK_SIZE ([FA] Backend
  * raises on block_size % 16 != 0), ATTN_ERR_GQA, ATTN_ERR_UNSUPPORTED (head_size not 64/128, unknown
- * dtype, partition_tokens not a multiple of 128 in [128, 4096], window > 0 without
+ * dtype, partition_tokens not a multiple of 128 in [128, 16384], window > 0 without
  * causal, scale not finite and > 0),
  * ATTN_ERR_WORKSPACE, ATTN_ERR_HIP (launch failure).
  */

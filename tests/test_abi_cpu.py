@@ -61,7 +61,7 @@ def _fwd(desc, causal=1, window=0, scale=0.125, ws=None, ws_bytes=0, q=FAKE, out
     (dict(head_size=96), A.ATTN_ERR_UNSUPPORTED),
     (dict(dtype=7), A.ATTN_ERR_UNSUPPORTED),
     (dict(partition_tokens=100), A.ATTN_ERR_UNSUPPORTED),
-    (dict(partition_tokens=4096 + 128), A.ATTN_ERR_UNSUPPORTED),
+    (dict(partition_tokens=16384 + 128), A.ATTN_ERR_UNSUPPORTED),
     (dict(num_decodes=3), A.ATTN_ERR_SHAPE),
     (dict(num_tokens=-1), A.ATTN_ERR_SHAPE),
     (dict(max_seq_len=49), A.ATTN_ERR_SHAPE),       # exceeds max_blocks_per_seq * block_size

@@ -116,6 +116,16 @@ DECODE_LENS = [1, 15, 16, 17, 511, 512, 513, 2047, 2048, 2049, 4095, 4096, 4097,
                300, 7777, 12345]
 
 
+def default_partition(num_decodes, num_heads, num_kv_heads, max_seq_len):
+    """The library's partition length for partition_tokens = 0 (include/attn.h): the longest
+    of 16384, 8192, ..., 256 giving at least 2048 split workgroups, else 256."""
+    per_part = num_decodes * num_kv_heads * -(-(num_heads // num_kv_heads) // 16)
+    P = 16384
+    while P > 256 and per_part * -(-max_seq_len // P) < 2048:
+        P //= 2
+    return P
+
+
 @pytest.mark.parametrize("window,part", [(0, 0), (0, 512), (3000, 0), (100, 1024)],
                          ids=["default", "p512", "w3000", "w100-p1024"])
 def test_decode_schedule_lists_every_partition_longest_first(window, part):
@@ -138,7 +148,7 @@ def test_decode_schedule_lists_every_partition_longest_first(window, part):
     torch.cuda.synchronize()
     # workspace layout of the C layer: partition results ([nd][Hq][max_parts][d] and
     # [nd][Hq][max_parts] fp32, padded to 256 bytes), then the schedule
-    P = part or 2048
+    P = part or default_partition(nd, 8, 2, b.max_seq_len)
     max_parts = -(-b.max_seq_len // P)
     if window > 0:
         max_parts = min(max_parts, -(-window // P) + 1)
