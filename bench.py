@@ -298,9 +298,10 @@ def fp8_decode_report(dev, seed):
     """Decode over an E4M3 cache (attn_fp8_decode_fwd) against the bf16 cache
     (attn_varlen_fwd) on the paged GQA decode workload (256 requests, contexts U[512, 8192],
     32 q / 8 kv heads, d 128, block 16) and on the mixed workload's 120 decode requests
-    (pass 0). Algorithmic bytes: each request's visible K and V once (2 bytes per element in
+    (pass 0), with the library's default partition (partition_tokens 0) and 2048, 4096 and
+    8192 keys. Algorithmic bytes: each request's visible K and V once (2 bytes per element in
     bf16, 1 in E4M3) plus q, out, lse and the block-table entries. One JSON line per
-    workload and cache type."""
+    workload, cache type and partition length."""
     import torch
     import exact_softmax_attention_paged_amd as A
     import gen
@@ -330,7 +331,7 @@ def fp8_decode_report(dev, seed):
                                  block_size=b.block_size,
                                  max_blocks_per_seq=b.max_blocks_per_seq, dtype=A.ATTN_BF16,
                                  partition_tokens=pt)
-                 for pt in (512, 1024, 2048)}
+                 for pt in (0, 2048, 4096, 8192)}
         # one workspace large enough for the shortest partitions (the most partials)
         ws = torch.empty(max(A.attn_workspace_bytes(dd) for dd in descs.values()),
                          dtype=torch.uint8, device=dev)

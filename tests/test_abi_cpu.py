@@ -320,3 +320,28 @@ def test_schedule_sizes_and_errors():
     assert lib.attn_varlen_fwd_scheduled(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 1,
                                          0, FAKE, None, FAKE, 1 << 20, None, 0, None) == \
         A.ATTN_ERR_WORKSPACE
+
+
+def test_default_partition_follows_the_batch_size():
+    """partition_tokens 0: the longest of 16384 ... 256 keys that still gives at least 2048
+    split workgroups (decodes x kv heads x head groups x partitions of max_seq_len), else 256
+    (include/attn.h); observed through the workspace size, which holds one partial result and
+    one schedule slot per (decode, partition)."""
+    def need(num_decodes, max_seq_len, heads=32, kv=8):
+        d = _desc(num_seqs=num_decodes, num_tokens=num_decodes, num_decodes=num_decodes,
+                  max_query_len=1, max_seq_len=max_seq_len, num_heads=heads, num_kv_heads=kv,
+                  num_blocks=num_decodes * 3000, max_blocks_per_seq=-(-max_seq_len // 16))
+        return A.attn_workspace_bytes(d)
+
+    def expected(decodes, parts, heads=32, d=128):
+        return (-(-(decodes * heads * parts * (d + 1) * 4) // 256) * 256 +
+                -(-((1 + decodes * parts) * 4) // 256) * 256)
+    # 256 requests x 8 kv heads = 2048 workgroups with one 16384-key partition each
+    assert need(256, 8192) == expected(256, 1)
+    # 120 x 8 = 960 per partition: 16384 keys give 1920 (< 2048), 8192 keys give 3840
+    assert need(120, 32768) == expected(120, 4)
+    # a single request of 40000 keys: 8 per partition, so the 256-key floor (157 partitions)
+    assert need(1, 40000) == expected(1, -(-40000 // 256))
+    # 64 q heads on one kv head form 4 workgroups of 16 heads: 64 x 4 = 256 per partition,
+    # so 1024-key partitions (8 of them) are the longest reaching 2048
+    assert need(64, 8192, heads=64, kv=1) == expected(64, 8, heads=64)
