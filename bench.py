@@ -458,11 +458,12 @@ def configs_report(dev, seed):
 def mixed_step(batch, layers, dev):
     """The timed step's launch configuration: per layer pass, the decode rows (split-KV kernel
     + LSE merge, their own descriptor) and the prefill rows (prefill kernel, query starts
-    rebased to 0). The two row sets are independent, so the decode calls go to a second
-    stream (default priority) forked from torch's current stream at the start of the step and
-    joined back at its end, while the prefill calls run on the current stream: the HBM-bound
-    decode kernels then run beside the MFMA-bound prefill kernels on the CUs the prefill
-    workgroups leave free. Returns step(ev=None) and the out / lse tensors it writes (one per
+    rebased to 0). Within a pass the two row sets are independent, so the decode call goes to
+    a second stream (default priority) forked from torch's current stream at the start of the
+    pass and joined back at its end, while the prefill call runs on the current stream: the
+    HBM-bound decode kernels then run beside the MFMA-bound prefill kernel on the CUs its
+    workgroups leave free. Passes do not overlap (a model's next layer needs this one's
+    output). Returns step(ev=None) and the out / lse tensors it writes (one per
     pass); with ev, step records ev[pass][0..1] around the decode call on the decode stream
     and ev[pass][2..3] around the prefill call on the current stream."""
     import torch
@@ -485,7 +486,7 @@ def mixed_step(batch, layers, dev):
     desc_pre = A.make_desc(num_seqs=batch.num_seqs - nd, num_tokens=batch.num_tokens - tok0,
                            num_decodes=0, max_query_len=int(batch.query_lens[nd:].max()),
                            max_seq_len=int(batch.seq_lens[nd:].max()), **common)
-    # one workspace per pass: the decode calls of both passes may be in flight together
+    # one decode workspace per pass
     wss = [torch.empty(A.attn_workspace_bytes(desc_dec), dtype=torch.uint8, device=dev)
            for _ in layers]
     outs = [torch.empty_like(q) for q, _ in layers]
@@ -496,26 +497,25 @@ def mixed_step(batch, layers, dev):
     fork, join = torch.cuda.Event(), torch.cuda.Event()
 
     def step(ev=None):
-        fork.record(stream)
-        dec_stream.wait_event(fork)            # the step's inputs are ready on both streams
         for li, (q, kv) in enumerate(layers):
             causal, window = batch.passes[li]
+            # a layer pass starts when the previous one has ended on both streams (a model's
+            # next layer needs this layer's output); within it the row sets overlap
+            fork.record(stream)
+            dec_stream.wait_event(fork)
             if ev is not None:
                 ev[li][0].record(dec_stream)
             A.attn_varlen_fwd(desc_dec, q[:nd], kv, bt_dec, qsl_dec, sl_dec, batch.scale,
                               causal, window, outs[li][:nd], lses[li][:nd], wss[li], dec_stream)
             if ev is not None:
                 ev[li][1].record(dec_stream)
-        for li, (q, kv) in enumerate(layers):
-            causal, window = batch.passes[li]
-            if ev is not None:
                 ev[li][2].record(stream)
             A.attn_varlen_fwd(desc_pre, q[tok0:], kv, bt_pre, qsl_pre, sl_pre, batch.scale,
                               causal, window, outs[li][tok0:], lses[li][tok0:], None, stream)
             if ev is not None:
                 ev[li][3].record(stream)
-        join.record(dec_stream)
-        stream.wait_event(join)                # the step ends when both row sets are done
+            join.record(dec_stream)
+            stream.wait_event(join)            # the pass ends when both row sets are done
 
     def prefill_call(li):
         """Layer pass li's prefill-rows call alone, on the current stream."""
