@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   constexpr int RS = D + 16;           // LDS row stride (bf16) of a V chunk
   constexpr int KC = D / 32;
   constexpr int DC = D / 16;
-  constexpr int TPR = D / 8;           // lanes per V row in the copy
+  constexpr int EPL = FP8 ? 16 : 8;    // V elements per lane and copy instruction (16 bytes)
+  constexpr int TPR = D / EPL;         // lanes per V row in the copy
   constexpr int RPI = kWave / TPR;     // V rows per copy instruction
   constexpr int NV = kChunk / RPI;     // copy instructions per chunk
   constexpr int V_TILE = kChunk * RS;  // bf16 per wave tile
@@ -134,13 +135,12 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   __syncthreads();   // sBlk ready
 
   // raw K / V of one chunk: bf16 K as MFMA operands, E4M3 K as each lane's D/4-byte strip
-  // (D/64 16-byte words); V as 16 bytes (bf16) or 8 bytes (E4M3) per lane and instruction
+  // (D/64 16-byte words); V as 16 bytes per lane and instruction (8 bf16 or 16 E4M3 codes)
   constexpr int KW = FP8 ? D / 64 : KC;
   constexpr int kInFlight = 2;
-  typedef typename std::conditional<FP8, u32x2, u32x4>::type vword_t;
   struct Chunk {
     u32x4 k[2][KW];
-    vword_t v[NV];
+    u32x4 v[NV];
   };
   // Element offset of the first row of the 16-key group starting at key g0 (clamped to the
   // last visible group, so every load below reads a valid row of this request). A 16-key
@@ -180,8 +180,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
       const int row = j * RPI + v_row;                 // row in the chunk; its 16-key group
       int g0;                                          // is uniform across the instruction
       const uint64_t base = group_off(kb + (j * RPI / 16) * 16, &g0);
-      ch.v[j] = *reinterpret_cast<const vword_t*>(
-          vcache + base + (uint32_t)(min(row % 16, last_key - g0) * kv_row + 8 * v_chunk));
+      ch.v[j] = *reinterpret_cast<const u32x4*>(
+          vcache + base + (uint32_t)(min(row % 16, last_key - g0) * kv_row + EPL * v_chunk));
     }
   };
 
@@ -196,10 +196,13 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
     const int kb = c_base + (c_first + ci) * kChunk;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      bf16x8 vv;
-      if constexpr (FP8) vv = fp8x8_to_bf16x8(ch.v[j][0], ch.v[j][1]);
-      else vv = __builtin_bit_cast(bf16x8, ch.v[j]);
-      *reinterpret_cast<bf16x8*>(&sVw[(j * RPI + v_row) * RS + 8 * v_chunk]) = vv;
+      __bf16* dst = &sVw[(j * RPI + v_row) * RS + EPL * v_chunk];
+      if constexpr (FP8) {
+        *reinterpret_cast<bf16x8*>(dst) = fp8x8_to_bf16x8(ch.v[j][0], ch.v[j][1]);
+        *reinterpret_cast<bf16x8*>(dst + 8) = fp8x8_to_bf16x8(ch.v[j][2], ch.v[j][3]);
+      } else {
+        *reinterpret_cast<bf16x8*>(dst) = __builtin_bit_cast(bf16x8, ch.v[j]);
+      }
     }
     floatx4 sc[2];
 #pragma unroll
