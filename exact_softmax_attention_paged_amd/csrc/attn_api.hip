@@ -169,8 +169,8 @@ attn::DecodeParams decode_params(const attn_desc& d, const attn::PrefillParams& 
   dp.num_decodes = d.num_decodes;
   dp.part_tokens = partition_tokens(&d);
   dp.max_parts = (int32_t)max_parts;
-  dp.schedule = reinterpret_cast<const int32_t*>(reinterpret_cast<char*>(ws) +
-                                                 decode_results_bytes(&d, max_parts));
+  dp.schedule = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
+                                           decode_results_bytes(&d, max_parts));
   dp.window = pp.window;
   dp.scale = pp.scale;
   dp.group_recip = pp.group_recip;

@@ -386,7 +386,7 @@ hipError_t launch(const DecodeParams& p, hipStream_t stream) {
   const int head_groups = (group + 15) / 16;
   DecodeScheduleParams sp{};
   sp.seq_lens = p.seq_lens;
-  sp.schedule = const_cast<int32_t*>(p.schedule);
+  sp.schedule = p.schedule;         // written here, read by the split kernel
   sp.num_decodes = p.num_decodes;
   sp.part_tokens = p.part_tokens;
   sp.max_parts = p.max_parts;

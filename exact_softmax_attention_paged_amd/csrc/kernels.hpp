@@ -65,7 +65,7 @@ struct DecodeParams {
   uint64_t group_recip;         // ceil(2^32 / (block_size / 16)), as in PrefillParams
   float v_scale;                // E4M3 cache only: V dequantisation scale (k_scale is folded
                                 // into scale by the host)
-  const int32_t* schedule;      // work items, longest first (see DecodeScheduleParams): grid
+  int32_t* schedule;            // work items, longest first (see DecodeScheduleParams): grid
                                 // x = item slot * (num_kv_heads * head groups) + kv head group
   // Cascade suffix pass (zero / null for a plain call):
   int32_t kv_skip_blocks;       // as in PrefillParams
