@@ -51,6 +51,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   constexpr int RPI = kWave / TPR;     // V rows per copy instruction
   constexpr int NV = kChunk / RPI;     // copy instructions per chunk
   constexpr int V_TILE = kChunk * RS;  // bf16 per wave tile
+  // bf16 K also goes through a wave-private LDS tile: its rows are loaded like V's (whole
+  // 256-byte rows, 4 per instruction), which streams about 9 % faster on gfx950 than loading
+  // the MFMA operand layout straight from HBM (16 rows x 64 bytes per instruction)
+  constexpr int KRS = D + 8;           // LDS row stride (bf16) of a K chunk
+  constexpr int K_TILE = kChunk * KRS;
   constexpr int OS = D + 4;            // fp32 row stride of the combine buffer
 
   // V tiles during the stream; reused as the combine buffer afterwards
@@ -60,6 +65,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   __shared__ float sM[kWaves][16];
   __shared__ float sL[kWaves][16];
   __shared__ int32_t sBlk[kMaxPartitionTokens / 16];   // block ids of this partition
+  __shared__ __attribute__((aligned(16))) __bf16 sK[FP8 ? 8 : kWaves * K_TILE];
 
   // grid x = item slot * heads_wg + (kv head, head group): the workgroups of one item read
   // the same tokens' rows (adjacent in every cache block) side by side, and the items come
@@ -130,13 +136,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
       w_end > w_begin ? (w_end - (c_base + c_first * kChunk) + kChunk - 1) / kChunk : 0;
 
   __bf16* sVw = reinterpret_cast<__bf16*>(lds) + w * V_TILE;
+  __bf16* sKw = sK + (FP8 ? 0 : w * K_TILE);
   const int v_row = lane / TPR;
   const int v_chunk = lane % TPR;
   __syncthreads();   // sBlk ready
 
-  // raw K / V of one chunk: bf16 K as MFMA operands, E4M3 K as each lane's D/4-byte strip
-  // (D/64 16-byte words); V as 16 bytes per lane and instruction (8 bf16 or 16 E4M3 codes)
+  // raw K / V of one chunk: bf16 K as whole rows like V (instruction j = k[j / KW][j % KW]),
+  // E4M3 K as each lane's D/4-byte strip (D/64 16-byte words); V as 16 bytes per lane and
+  // instruction (8 bf16 or 16 E4M3 codes)
   constexpr int KW = FP8 ? D / 64 : KC;
+  static_assert(FP8 || 2 * KW == NV, "bf16 K rows use the V copy's instruction count");
   constexpr int kInFlight = 2;
   struct Chunk {
     u32x4 k[2][KW];
@@ -161,18 +170,23 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   // keys past the wave's range load a valid row (clamped); their scores are masked, so they
   // add 0 * (finite V) and need no zeroing
   auto load_chunk = [&](Chunk& ch, int kb) {
+    if constexpr (FP8) {
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      int g0;
-      const uint64_t base = group_off(kb + 16 * t2, &g0);
-      if constexpr (FP8) {
+      for (int t2 = 0; t2 < 2; ++t2) {
+        int g0;
+        const uint64_t base = group_off(kb + 16 * t2, &g0);
         const kv_t* src = kcache + base + (uint32_t)(min(li, last_key - g0) * kv_row + (D / 4) * G);
 #pragma unroll
         for (int c = 0; c < KW; ++c) ch.k[t2][c] = *reinterpret_cast<const u32x4*>(src + 16 * c);
-      } else {
-        const kv_t* src = kcache + base + (uint32_t)(min(li, last_key - g0) * kv_row + 8 * G);
+      }
+    } else {
 #pragma unroll
-        for (int c = 0; c < KC; ++c) ch.k[t2][c] = *reinterpret_cast<const u32x4*>(src + 32 * c);
+      for (int j = 0; j < NV; ++j) {
+        const int row = j * RPI + v_row;               // as for V below
+        int g0;
+        const uint64_t base = group_off(kb + (j * RPI / 16) * 16, &g0);
+        ch.k[j / KW][j % KW] = *reinterpret_cast<const u32x4*>(
+            kcache + base + (uint32_t)(min(row % 16, last_key - g0) * kv_row + EPL * v_chunk));
       }
     }
 #pragma unroll
@@ -204,6 +218,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
         *reinterpret_cast<bf16x8*>(dst) = __builtin_bit_cast(bf16x8, ch.v[j]);
       }
     }
+    if constexpr (!FP8) {
+      // K rows into the K tile; once both tiles are written the chunk's registers are free,
+      // so the chunk after next is requested before the MFMAs
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+        *reinterpret_cast<bf16x8*>(&sKw[(j * RPI + v_row) * KRS + EPL * v_chunk]) =
+            __builtin_bit_cast(bf16x8, ch.k[j / KW][j % KW]);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the writes land before any read
+      if (ci + kInFlight < n_chunks) load_chunk(ch, kb + kInFlight * kChunk);
+    }
     floatx4 sc[2];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
@@ -213,13 +237,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
         bf16x8 ka;
         if constexpr (FP8)
           ka = fp8x8_to_bf16x8(ch.k[t2][c / 2][2 * (c % 2)], ch.k[t2][c / 2][2 * (c % 2) + 1]);
-        else
-          ka = __builtin_bit_cast(bf16x8, ch.k[t2][c]);
+        else   // the A operand: lane (G, li) holds key 16 t2 + li, d = 32c + 8G .. +7
+          ka = *reinterpret_cast<const bf16x8*>(&sKw[(16 * t2 + li) * KRS + 32 * c + 8 * G]);
         acc = mfma16x16x32(ka, qf[c], acc);
       }
       sc[t2] = acc;
     }
-    if (ci + kInFlight < n_chunks) load_chunk(ch, kb + kInFlight * kChunk);
+    if constexpr (FP8) {
+      if (ci + kInFlight < n_chunks) load_chunk(ch, kb + kInFlight * kChunk);
+    }
     if (kb < w_begin || kb + kChunk > w_end) {
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
