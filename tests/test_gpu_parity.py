@@ -11,8 +11,9 @@ import numpy as np
 import pytest
 import torch
 
+import exact_softmax_attention_paged_amd as A
 import gen
-from parity import compare, oracle_on, run_library
+from parity import compare, device_meta, oracle_on, run_library
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -182,3 +183,32 @@ def test_many_tiny_decodes():
     out, lse = run_library(b, q, kv, True, 0)
     ref_out, ref_lse = oracle_on(b, q, kv, True, 0)
     print(compare(out, lse, ref_out, ref_lse, label="tiny decodes"))
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 37)],
+                         ids=["noncausal", "causal", "w37"])
+def test_requests_without_queries_write_nothing(causal, window):
+    """Requests with query_len 0 (a context but no new token, or nothing at all) sit between
+    decode and prefill requests: they own no output row, and every other row still matches
+    the oracle. The rows of the whole output are checked, and a sentinel shows that nothing
+    outside them is written."""
+    b = _batch(88, ql=[1, 1, 0, 300, 0, 5, 0], sl=[100, 2000, 500, 300, 0, 900, 17], hq=8,
+               hkv=2, d=128, bs=16)
+    print(f"[case] zero-length queries causal={causal} window={window}", flush=True)
+    q, kv = gen.make_tensors(b, 88, DEV, poison=True)
+    bt, qsl, sl = device_meta(b, DEV)
+    desc = A.make_desc(num_seqs=b.num_seqs, num_tokens=b.num_tokens, num_decodes=b.num_decodes,
+                       max_query_len=b.max_query_len, max_seq_len=b.max_seq_len, num_heads=8,
+                       num_kv_heads=2, head_size=128, num_blocks=b.num_blocks, block_size=16,
+                       max_blocks_per_seq=b.max_blocks_per_seq, dtype=A.ATTN_BF16)
+    ws = torch.empty(A.attn_workspace_bytes(desc), dtype=torch.uint8, device=DEV)
+    # one sentinel row beyond the last token in both outputs
+    out_full = torch.full((b.num_tokens + 1, 8, 128), 7.0, dtype=q.dtype, device=DEV)
+    lse_full = torch.full((b.num_tokens + 1, 8), 7.0, dtype=torch.float32, device=DEV)
+    A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl, b.scale, causal, window,
+                      out_full[:b.num_tokens], lse_full[:b.num_tokens], ws)
+    torch.cuda.synchronize()
+    assert bool((out_full[b.num_tokens] == 7.0).all()) and bool((lse_full[b.num_tokens] == 7.0).all())
+    ref_out, ref_lse = oracle_on(b, q, kv, causal, window)
+    compare(out_full[:b.num_tokens], lse_full[:b.num_tokens], ref_out, ref_lse,
+            label="zero-length queries")
