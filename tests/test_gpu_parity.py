@@ -34,6 +34,11 @@ SMALL = [
                                            hq=16, hkv=2, d=128, bs=16)),
     ("decode-d64-gqa20", dict(ql=[1, 1, 1], sl=[513, 2000, 64], hq=40, hkv=2, d=64, bs=64)),
     ("decode-d128-g1-bs512", dict(ql=[1, 1, 9], sl=[1025, 511, 520], hq=3, hkv=3, d=128, bs=512)),
+    # block sizes that are multiples of 16 but not powers of two (block index by reciprocal)
+    ("mixed-d128-gqa4-bs48", dict(ql=[1, 1, 200, 37], sl=[1000, 50, 700, 400], hq=8, hkv=2,
+                                  d=128, bs=48)),
+    ("mixed-d64-gqa4-bs80", dict(ql=[1, 150, 3], sl=[3000, 1500, 81], hq=4, hkv=1, d=64,
+                                 bs=80)),
 ]
 MASKS = [(False, 0), (True, 0), (True, 1), (True, 100), (True, 513)]
 
