@@ -550,8 +550,8 @@ def main():
         record_traffic(args.record_traffic[0], args.record_traffic[1], args.record_command)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: the attention kernels run on one device and "
+              "there is no multi-GPU launch (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
