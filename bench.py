@@ -455,6 +455,33 @@ def configs_report(dev, seed):
         torch.cuda.empty_cache()
 
 
+def ceilings_report(dev):
+    """What this device delivers outside the attention kernels, beside the spec peaks the
+    roofline fractions use: a bf16 GEMM through torch.mm (the vendor BLAS; 8192 x 8192 x 8192,
+    contiguous operands) as the attainable MFMA rate, and a 4 GiB device-to-device copy
+    (read + write bytes) as an attainable HBM rate. One JSON line each."""
+    import torch
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    ms = _time_ms(lambda: torch.mm(a, b, out=c), 20)
+    flops = 2.0 * n * n * n
+    print(json.dumps({"report": "ceilings", "what": "bf16 GEMM 8192^3 (torch.mm)",
+                      "ms": round(ms, 4), "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+                      "frac_of_spec": round(flops / (ms / 1e3) / PEAK_BF16_FLOPS, 4)}),
+          flush=True)
+    del a, b, c
+    src = torch.empty(1 << 30, device=dev, dtype=torch.int32)
+    dst = torch.empty_like(src)
+    ms = _time_ms(lambda: dst.copy_(src), 20)
+    byts = 2.0 * src.numel() * 4
+    print(json.dumps({"report": "ceilings", "what": "4 GiB device copy (read + write)",
+                      "ms": round(ms, 4), "gbps": round(byts / (ms / 1e3) / 1e9, 1),
+                      "frac_of_spec": round(byts / (ms / 1e3) / PEAK_HBM_BYTES, 4)}),
+          flush=True)
+
+
 def mixed_step(batch, layers, dev):
     """The timed step's launch configuration: per layer pass, the decode rows (split-KV kernel
     + LSE merge, their own descriptor) and the prefill rows (prefill kernel, query starts
@@ -542,7 +569,7 @@ def main():
                     help="write profiles/prefill_traffic.json from two rocprofv3 --pmc runs")
     ap.add_argument("--record-command", default="", help="command line stored with the record")
     ap.add_argument("--report", choices=["configs", "cascade", "kv-write", "fp8-decode",
-                                         "schedule"],
+                                         "schedule", "ceilings"],
                     help="instead of the headline step, time one of the next-step paths "
                          "against the plain path and print one JSON line per batch")
     args = ap.parse_args()
@@ -579,6 +606,9 @@ def main():
         return
     if args.report == "schedule":
         schedule_report(dev, args.seed)
+        return
+    if args.report == "ceilings":
+        ceilings_report(dev)
         return
     batch = gen.config(5, seed=args.seed)
     layers = [gen.make_tensors(batch, args.seed, dev, layer=li) for li in range(len(batch.passes))]
