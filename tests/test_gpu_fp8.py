@@ -54,6 +54,7 @@ DECODE = [
     ("d128-gqa8-bs16", dict(sl=[1, 17, 700, 1500, 4097], hq=16, hkv=2, d=128, bs=16)),
     ("d64-gqa20-bs64", dict(sl=[513, 2000, 64], hq=40, hkv=2, d=64, bs=64)),
     ("d128-mha-bs32", dict(sl=[33, 1025, 300], hq=4, hkv=4, d=128, bs=32)),
+    ("d128-gqa4-bs48", dict(sl=[47, 49, 1000, 3000], hq=8, hkv=2, d=128, bs=48)),
 ]
 
 
