@@ -114,12 +114,13 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   const kv_t* __restrict__ vcache = kcache + p.v_offset;
 
   // Q^T (B operand): lane (G, li) holds q head h0 + li at the d values its K operand holds:
-  // d = 32c + 8G .. +7 (bf16), or d = (D/4)G + 8c .. +7 for E4M3 K, where each lane reads one
-  // contiguous D/4-byte strip of the row (any fixed order of d is the same dot product)
+  // d = 32c + 8G .. +7 (bf16), or d = 64(c/2) + 16G + 8(c%2) .. +7 for E4M3 K, where lane G
+  // reads bytes 64w + 16G .. +15 of the row with load w, so that each load instruction covers
+  // 64 contiguous bytes of 16 rows (any fixed order of d is the same dot product)
   bf16x8 qf[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
-    const int d0 = FP8 ? (D / 4) * G + 8 * c : 32 * c + 8 * G;
+    const int d0 = FP8 ? 64 * (c / 2) + 16 * G + 8 * (c % 2) : 32 * c + 8 * G;
     qf[c] = li < nh ? *reinterpret_cast<const bf16x8*>(
                           q + ((int64_t)tok * p.num_heads + h0 + li) * D + d0)
                     : bf16x8{};
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   __syncthreads();   // sBlk ready
 
   // raw K / V of one chunk: bf16 K as whole rows like V (instruction j = k[j / KW][j % KW]),
-  // E4M3 K as each lane's D/4-byte strip (D/64 16-byte words); V as 16 bytes per lane and
+  // E4M3 K as D/64 16-byte words per lane (word w at byte 64w + 16G); V as 16 bytes per lane and
   // instruction (8 bf16 or 16 E4M3 codes)
   constexpr int KW = FP8 ? D / 64 : KC;
   static_assert(FP8 || 2 * KW == NV, "bf16 K rows use the V copy's instruction count");
@@ -175,9 +176,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
       for (int t2 = 0; t2 < 2; ++t2) {
         int g0;
         const uint64_t base = group_off(kb + 16 * t2, &g0);
-        const kv_t* src = kcache + base + (uint32_t)(min(li, last_key - g0) * kv_row + (D / 4) * G);
+        const kv_t* src = kcache + base + (uint32_t)(min(li, last_key - g0) * kv_row + 16 * G);
 #pragma unroll
-        for (int c = 0; c < KW; ++c) ch.k[t2][c] = *reinterpret_cast<const u32x4*>(src + 16 * c);
+        for (int c = 0; c < KW; ++c) ch.k[t2][c] = *reinterpret_cast<const u32x4*>(src + 64 * c);
       }
     } else {
 #pragma unroll
