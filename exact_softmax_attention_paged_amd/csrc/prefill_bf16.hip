@@ -40,6 +40,16 @@ namespace {
 
 constexpr int kRows = 32;     // query rows per wave
 constexpr float kRescaleLog2 = 8.f;
+// Maximum of scores, which hold no NaN: IEEE maximum (v_maximum3_f32 on gfx950) needs no
+// quieting of its operands, whereas fmaxf first canonicalises each MFMA result that it cannot
+// prove canonical (one more v_max per operand).
+__device__ __forceinline__ float max3_f32(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+__device__ __forceinline__ float max_f32(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 constexpr int kWaves = 8;                    // waves per workgroup (2 per SIMD)
 // Keys per KV tile: 128 for d = 128 (half the per-tile overhead: barrier, row-max reduction,
 // load issue), 64 for d = 64, whose short, ragged sequences waste more of a long tile
@@ -428,17 +438,28 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
       // online softmax with a lazily moved reference max, one query column per lane pair;
       // the row max and row sum use 8 independent partial results (short dependency
       // chains) combined by a tree
+      // (each chain starts from three scores and takes two more per three-input maximum)
       float pm[8];
+      {
+        constexpr int NS = 16 * kKT;                 // scores per lane
+#define SC(n) sc[(n) / 16][(n) % 16]
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pm[i] = __builtin_fmaxf(sc[0][2 * i], sc[0][2 * i + 1]);
+        for (int i = 0; i < 8; ++i) pm[i] = max3_f32(SC(3 * i), SC(3 * i + 1), SC(3 * i + 2));
 #pragma unroll
-      for (int x = 16; x < 16 * kKT; x += 16)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          pm[i] = __builtin_fmaxf(__builtin_fmaxf(pm[i], sc[x / 16][2 * i]), sc[x / 16][2 * i + 1]);
-      float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(pm[0], pm[1]), __builtin_fmaxf(pm[2], pm[3])),
-                                 __builtin_fmaxf(__builtin_fmaxf(pm[4], pm[5]), __builtin_fmaxf(pm[6], pm[7])));
-      mx = max_xor32(mx);
+        for (int n = 24; n + 1 < NS; n += 2) {
+          const int i = ((n - 24) / 2) % 8;
+          pm[i] = max3_f32(pm[i], SC(n), SC(n + 1));
+        }
+        if constexpr (NS % 2 == 1) pm[0] = max_f32(pm[0], SC(NS - 1));
+#undef SC
+      }
+      float mx = max3_f32(max3_f32(pm[0], pm[1], pm[2]), max3_f32(pm[3], pm[4], pm[5]),
+                          max_f32(pm[6], pm[7]));
+      {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                  false, false);
+        mx = max_f32(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      }
       // move the reference when the tile max exceeds it by more than 2^kRescaleLog2
       // (always on a column's first visible key, where m_ref is -inf)
       const bool move = (mx - m_ref) * c_log2 > kRescaleLog2;
