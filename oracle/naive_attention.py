@@ -102,7 +102,10 @@ def attention(q: np.ndarray, kv_cache: np.ndarray, block_table: np.ndarray,
     returns   out float64 [num_tokens, num_heads, head_size], lse float64 [num_tokens, num_heads]
 
     ``rows`` restricts the work to the listed token indices; other rows are NaN. Rows are
-    independent by definition, so they are processed in chunks of ``row_chunk``.
+    independent by definition, so they are processed in chunks: for each kv head, the
+    (query, q head) rows of its GQA group go through attend_rows together, at most
+    ``row_chunk`` of them at a time (each row's scores, softmax and x V are its own; sharing
+    one product only saves re-reading that kv head's keys per q head).
     """
     num_tokens, num_heads, head_size = q.shape
     num_kv_heads = kv_cache.shape[3]
@@ -124,14 +127,19 @@ def attention(q: np.ndarray, kv_cache: np.ndarray, block_table: np.ndarray,
             continue
         k, v = gather_kv(kv_cache, block_table[r], sl)
         vis_all = visible_keys(ql, sl, causal, window)
-        for c0 in range(0, idx.size, row_chunk):
-            ii = idx[c0:c0 + row_chunk]
-            vis = vis_all[ii]
-            for h in range(num_heads):
-                kvh = h // group
-                o, ls = attend_rows(q[q0 + ii, h], k[:, kvh], v[:, kvh], scale, vis)
-                out[q0 + ii, h] = o
-                lse[q0 + ii, h] = ls
+        step = max(1, row_chunk // group)
+        for kvh in range(num_kv_heads):
+            heads = np.arange(kvh * group, (kvh + 1) * group)   # q head h reads kv head h // group
+            k_h = np.ascontiguousarray(k[:, kvh])
+            v_h = np.ascontiguousarray(v[:, kvh])
+            for c0 in range(0, idx.size, step):
+                ii = idx[c0:c0 + step]
+                # rows (query i, q head h) of this group, query-major
+                q_rows = q[q0 + ii][:, heads].reshape(ii.size * group, head_size)
+                vis = np.repeat(vis_all[ii], group, axis=0)
+                o, ls = attend_rows(q_rows, k_h, v_h, scale, vis)
+                out[np.ix_(q0 + ii, heads)] = o.reshape(ii.size, group, head_size)
+                lse[np.ix_(q0 + ii, heads)] = ls.reshape(ii.size, group)
     return out, lse
 
 

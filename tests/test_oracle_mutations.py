@@ -17,14 +17,15 @@ MUTATIONS = {
     "top_left_causal": ("p = context_len + np.arange(query_len)[:, None]",
                         "p = np.arange(query_len)[:, None]"),
     "lse_without_max": ("m_safe + np.log", "np.log"),
-    "kv_head_modulo": ("kvh = h // group", "kvh = h % num_kv_heads"),
+    "kv_head_modulo": ("heads = np.arange(kvh * group, (kvh + 1) * group)",
+                       "heads = np.arange(kvh, num_heads, num_kv_heads)"),
     "v_read_from_k": ("v = np.asarray(kv_cache[1]", "v = np.asarray(kv_cache[0]"),
     "slot_shifted": ("slots = t % block_size", "slots = (t + 1) % block_size"),
     "exp_sign": ("np.exp(s - m_safe)", "np.exp(m_safe - s)"),
     "unnormalised": ("e / np.where(empty, 1.0, l)", "e"),
     "values_key_order_reversed": ("return w @ np.asarray(v, np.float64), lse",
                                   "return w @ np.asarray(v, np.float64)[::-1], lse"),
-    "query_rows_misaligned": ("o, ls = attend_rows(q[q0 + ii, h]", "o, ls = attend_rows(q[ii, h]"),
+    "query_rows_misaligned": ("q_rows = q[q0 + ii][:, heads]", "q_rows = q[ii][:, heads]"),
 }
 
 
