@@ -82,6 +82,7 @@ def cpu_baseline(batch, layers, seed):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
+    cpu_model = host_cpu_model()
     nd = batch.num_decodes
     dec = list(range(0, nd, CPU_DECODE_STEP))
     pre = list(range(nd, batch.num_seqs))
@@ -116,12 +117,26 @@ def cpu_baseline(batch, layers, seed):
             byts += (sl - lo) * 2 * sub.num_kv_heads * d * 2
         floor_s += flops / PEAK_BF16_FLOPS + byts / PEAK_HBM_BYTES
     return {"value": 100.0 * floor_s / cpu_s, "unit": "% of MI355X roofline", "cores": threads,
-            "kind": "oracle", "seconds": round(cpu_s, 3),
+            "kind": "oracle", "seconds": round(cpu_s, 3), "cpu_model": cpu_model,
+            "host_logical_cpus": os.cpu_count(),
+            "threads_note": "cores = the BLAS thread pool the fp64 matrix products ran on (the "
+                            "rest of the oracle is single-threaded numpy)",
             "sample": f"fp64 numpy oracle; per layer pass: decode requests {dec[0]}..{dec[-1]} "
                       f"step {CPU_DECODE_STEP} ({len(dec)} of {nd}) and {CPU_PREFILL_ROWS} evenly "
                       f"spaced query rows of each of the {len(pre)} prefill requests, all "
                       f"{batch.num_heads} q heads; value = GPU-roofline time of that work / CPU "
                       f"time"}
+
+
+def host_cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (the box the oracle runs on)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
@@ -407,14 +422,21 @@ def schedule_report(dev, seed):
                           "scheduled_tflops": round(f / (ts / 1e3) / 1e12, 1)}), flush=True)
 
 
+COLD_ROTATION_BYTES = 512 << 20
+
+
 def configs_report(dev, seed):
     """Every workload (the tiny fp32 case, the BERT-large-shaped encoder, the GPT-2-shaped
     varlen prefill, the paged GQA decode, the mixed long-context batch) through one plain
-    attn_varlen_fwd call per layer pass, with the library's default decode partition. One
-    JSON line per (workload, pass): mean call time by HIP events, the algorithmic prefill
-    TFLOP/s and decode GB/s of that call, and its % of the MI355X roofline, (prefill flops /
-    MFMA peak + decode bytes / 8 TB/s) / call time, the MFMA peak being fp32 (157.3 TFLOP/s)
-    for the fp32 case and bf16 otherwise. The seed argument is unused: workload k has seed k."""
+    attn_varlen_fwd call per layer pass, with the library's default decode partition, and the
+    paged GQA decode again at its stated 512-token partitions. One JSON line per (workload,
+    pass, partition): mean call time by HIP events with the inputs hot in the caches, the
+    algorithmic prefill TFLOP/s and decode GB/s of that call, and its % of the MI355X roofline,
+    (prefill flops / MFMA peak + decode bytes / 8 TB/s) / call time, the MFMA peak being fp32
+    (157.3 TFLOP/s) for the fp32 case and bf16 otherwise. The three small prefill workloads are
+    also timed cold: the calls rotate over enough copies of q, the cache and the outputs (at
+    least 512 MiB, twice the 256 MiB last-level cache) that no call finds its inputs in a cache.
+    The seed argument is unused: workload k has seed k."""
     import torch
     import exact_softmax_attention_paged_amd as A
     import gen
@@ -422,45 +444,159 @@ def configs_report(dev, seed):
     for k in (1, 2, 3, 4, 5):
         b = gen.config(k)
         fp32 = b.dtype == "f32"
-        desc = A.make_desc(num_seqs=b.num_seqs, num_tokens=b.num_tokens,
-                           num_decodes=b.num_decodes, max_query_len=b.max_query_len,
-                           max_seq_len=b.max_seq_len, num_heads=b.num_heads,
-                           num_kv_heads=b.num_kv_heads, head_size=b.head_size,
-                           num_blocks=b.num_blocks, block_size=b.block_size,
-                           max_blocks_per_seq=b.max_blocks_per_seq,
-                           dtype=A.ATTN_F32 if fp32 else A.ATTN_BF16)
+        parts = [0, 512] if k == 4 else [0]
         bt, qsl, sl = (torch.from_numpy(x).to(dev) for x in (b.block_table, b.query_start_loc,
                                                              b.seq_lens))
-        ws = torch.empty(max(A.attn_workspace_bytes(desc), 1), dtype=torch.uint8, device=dev)
-        for li, (causal, window) in enumerate(b.passes):
-            q, kv = gen.make_tensors(b, k, dev, layer=li)
-            out = torch.empty_like(q)
-            lse = torch.empty(b.num_tokens, b.num_heads, dtype=torch.float32, device=dev)
-            reps = 10 if b.num_tokens > 10000 else 100
-            t = _time_ms(lambda: A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl, b.scale, causal,
-                                                   window, out, lse, ws), reps)
-            flops, dec_unique, dec_logical = algorithmic_work(b, causal, window)
-            peak = 157.3e12 if fp32 else PEAK_BF16_FLOPS
-            sec = t / 1e3
-            print(json.dumps({
-                "report": "configs", "workload": gen.CONFIG_NAMES[k], "pass": li,
-                "causal": causal, "window": window, "dtype": b.dtype, "call_ms": round(t, 4),
-                "prefill_gflop": round(flops / 1e9, 3),
-                "prefill_tflops": round(flops / sec / 1e12, 1) if flops else None,
-                "decode_gb_unique": round(dec_unique / 1e9, 4) if b.num_decodes else None,
-                "decode_gbps": round(dec_unique / sec / 1e9, 1) if b.num_decodes else None,
-                "pct_of_roofline": round(100 * (flops / peak + dec_unique / PEAK_HBM_BYTES) / sec,
-                                         2)}), flush=True)
-            del q, kv, out, lse
+        for pt in parts:
+            desc = A.make_desc(num_seqs=b.num_seqs, num_tokens=b.num_tokens,
+                               num_decodes=b.num_decodes, max_query_len=b.max_query_len,
+                               max_seq_len=b.max_seq_len, num_heads=b.num_heads,
+                               num_kv_heads=b.num_kv_heads, head_size=b.head_size,
+                               num_blocks=b.num_blocks, block_size=b.block_size,
+                               max_blocks_per_seq=b.max_blocks_per_seq,
+                               dtype=A.ATTN_F32 if fp32 else A.ATTN_BF16, partition_tokens=pt)
+            ws = torch.empty(max(A.attn_workspace_bytes(desc), 1), dtype=torch.uint8, device=dev)
+            for li, (causal, window) in enumerate(b.passes):
+                q, kv = gen.make_tensors(b, k, dev, layer=li)
+                out = torch.empty_like(q)
+                lse = torch.empty(b.num_tokens, b.num_heads, dtype=torch.float32, device=dev)
+                reps = 10 if b.num_tokens > 10000 else 100
+                t = _time_ms(lambda: A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl, b.scale,
+                                                       causal, window, out, lse, ws), reps)
+                flops, dec_unique, dec_logical = algorithmic_work(b, causal, window)
+                peak = 157.3e12 if fp32 else PEAK_BF16_FLOPS
+                rec = {"report": "configs", "workload": gen.CONFIG_NAMES[k], "pass": li,
+                       "causal": causal, "window": window, "dtype": b.dtype,
+                       "partition_tokens": pt if b.num_decodes else None,
+                       "partition_tokens_used": A.attn_decode_partition_tokens(desc)
+                       if b.num_decodes else None,
+                       "call_ms": round(t, 4), "prefill_gflop": round(flops / 1e9, 3)}
+                rec.update(_rates(t, flops, dec_unique if b.num_decodes else 0, peak))
+                if k <= 3:
+                    rec["cold"] = _cold_rates(A, b, desc, k, li, causal, window, bt, qsl, sl,
+                                              ws, flops, peak, dev)
+                print(json.dumps(rec), flush=True)
+                del q, kv, out, lse
+            del ws
         torch.cuda.empty_cache()
+
+
+def _rates(ms, flops, dec_bytes, peak):
+    sec = ms / 1e3
+    return {"prefill_tflops": round(flops / sec / 1e12, 1) if flops else None,
+            "decode_gb_unique": round(dec_bytes / 1e9, 4) if dec_bytes else None,
+            "decode_gbps": round(dec_bytes / sec / 1e9, 1) if dec_bytes else None,
+            "pct_of_roofline": round(100 * (flops / peak + dec_bytes / PEAK_HBM_BYTES) / sec, 2)}
+
+
+def _cold_rates(A, b, desc, k, li, causal, window, bt, qsl, sl, ws, flops, peak, dev):
+    """Mean call time over calls that each use the next of N copies of the inputs and outputs
+    (N copies >= COLD_ROTATION_BYTES), after one warm-up pass over all copies."""
+    import torch
+    import gen
+    q0, kv0 = gen.make_tensors(b, k, dev, layer=li)
+    per_set = (q0.numel() * 2 + kv0.numel()) * q0.element_size() + b.num_tokens * b.num_heads * 4
+    n = max(2, -(-COLD_ROTATION_BYTES // per_set))
+    sets = [(q0.clone(), kv0.clone(), torch.empty_like(q0),
+             torch.empty(b.num_tokens, b.num_heads, dtype=torch.float32, device=dev))
+            for _ in range(n)]
+    del q0, kv0
+
+    def call(i):
+        q, kv, out, lse = sets[i % n]
+        A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl, b.scale, causal, window, out, lse, ws)
+    for i in range(n):
+        call(i)
+    torch.cuda.synchronize()
+    reps = 4 * n
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    res = {"input_sets": n, "rotation_mib": round(n * per_set / 2**20, 1), "call_ms": round(ms, 4)}
+    res.update(_rates(ms, flops, 0, peak))
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+_probes = None
+
+
+def probes():
+    """libattn_probes.so (include/attn_probes.h): the HBM read stream and MFMA loop probes."""
+    global _probes
+    if _probes is None:
+        import ctypes
+        import torch  # noqa: F401  (the HIP runtime torch uses, loaded first)
+        path = os.path.join(ROOT, "exact_softmax_attention_paged_amd", "libattn_probes.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build with "
+                               "`python -m exact_softmax_attention_paged_amd.build`")
+        L = ctypes.CDLL(path)
+        vp, i32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64
+        L.attn_probe_read_stream.argtypes = [vp, u64, vp, i32, vp]
+        L.attn_probe_read_stream.restype = i32
+        L.attn_probe_mfma_loop.argtypes = [vp, vp, i32, i32, vp]
+        L.attn_probe_mfma_loop.restype = i32
+        _probes = L
+    return _probes
+
+
+def mfma_probe(dev, workgroups=256, iters=20000, reps=3):
+    """Run the MFMA loop probe: returns (TFLOP/s, mean shader clock in MHz under that load)."""
+    import ctypes
+    import torch
+    clocks = torch.zeros(4 * workgroups, dtype=torch.int64, device=dev)
+    sink = torch.zeros(8 * workgroups, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def run():
+        assert probes().attn_probe_mfma_loop(clocks.data_ptr(), sink.data_ptr(), workgroups,
+                                             iters, stream) == 0
+    ms = _time_ms(run, reps, warmup=1)
+    c = clocks.view(workgroups, 4).cpu().numpy().astype(np.float64)
+    mhz = float(np.median((c[:, 1] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 2], 1.0) * 100.0))
+    flops = workgroups * 8.0 * iters * 4 * 32768
+    return flops / (ms / 1e3) / 1e12, mhz
 
 
 def ceilings_report(dev):
     """What this device delivers outside the attention kernels, beside the spec peaks the
-    roofline fractions use: a bf16 GEMM through torch.mm (the vendor BLAS; 8192 x 8192 x 8192,
-    contiguous operands) as the attainable MFMA rate, and a 4 GiB device-to-device copy
-    (read + write bytes) as an attainable HBM rate. One JSON line each."""
+    roofline fractions use. Own probes (libattn_probes.so, the instruction forms the kernels
+    use): a 4 GiB HBM read stream of 16-byte loads at several grid sizes, and back-to-back
+    v_mfma_f32_32x32x16_bf16 (8 waves per workgroup, 4 independent accumulators per wave) with
+    the shader clock under that load. Vendor paths beside them: a bf16 GEMM through torch.mm
+    (8192 x 8192 x 8192, contiguous operands) and a 4 GiB device-to-device copy (read + write
+    bytes). One JSON line each."""
+    import ctypes
     import torch
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    src = torch.ones(1 << 30, device=dev, dtype=torch.int32)           # 4 GiB
+    for wgs in (1024, 2048, 4096, 8192, 16384):
+        sink = torch.empty(wgs * 256, device=dev, dtype=torch.int32)
+        ms = _time_ms(lambda: probes().attn_probe_read_stream(
+            src.data_ptr(), src.numel() * 4, sink.data_ptr(), wgs, stream), 10)
+        byts = src.numel() * 4.0
+        print(json.dumps({"report": "ceilings", "what": f"own HBM read stream, 4 GiB, 16-byte "
+                          f"loads, {wgs} workgroups x 256 threads",
+                          "ms": round(ms, 4), "gbps": round(byts / (ms / 1e3) / 1e9, 1),
+                          "frac_of_spec": round(byts / (ms / 1e3) / PEAK_HBM_BYTES, 4)}),
+              flush=True)
+    del src
+    for wgs in (256, 512):
+        tflops, mhz = mfma_probe(dev, wgs, 20000)
+        print(json.dumps({"report": "ceilings", "what": f"own v_mfma_f32_32x32x16_bf16 loop, "
+                          f"{wgs} workgroups x 8 waves, 4 independent accumulators per wave",
+                          "tflops": round(tflops, 1),
+                          "frac_of_spec": round(tflops * 1e12 / PEAK_BF16_FLOPS, 4),
+                          "shader_clock_mhz": round(mhz, 1),
+                          "frac_of_peak_at_that_clock": round(
+                              tflops * 1e12 / (PEAK_BF16_FLOPS * mhz / 2400.0), 4)}),
+              flush=True)
     n = 8192
     a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
     b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
@@ -656,6 +792,15 @@ def main():
     torch.cuda.synchronize()
     alone_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in alone]))
     achieved_alone = flops0 / (alone_ms / 1e3) / 1e12
+    # the shader clock under a full MFMA load (own probe, right after the timed region): the
+    # 2.5 PFLOP/s spec assumes 2.4 GHz, and the chip runs MFMA-bound kernels below that
+    try:
+        probe_tflops, sclk_mhz = mfma_probe(dev, 256, 20000)
+    except Exception as exc:          # the probes library is optional for the headline line
+        print(f"mfma probe unavailable: {exc}", file=sys.stderr)
+        probe_tflops, sclk_mhz = None, None
+    pre_frac = flops / (pre_ms / 1e3) / PEAK_BF16_FLOPS
+    dec_frac = dbytes_u / (dec_ms / 1e3) / PEAK_HBM_BYTES
     rec = {
         "metric": METRIC, "value": round(value, 3), "unit": "% of roofline",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -671,6 +816,12 @@ def main():
         "decode_gbps": round(dbytes_u / (dec_ms / 1e3) / 1e9, 1),
         "decode_gbps_logical": round(dbytes_l / (dec_ms / 1e3) / 1e9, 1),
         "prefill_ms_per_step": round(pre_ms, 4), "decode_ms_per_step": round(dec_ms, 4),
+        "prefill_frac": round(pre_frac, 4), "prefill_frac_target": 0.50,
+        "decode_frac": round(dec_frac, 4), "decode_frac_target": 0.70,
+        "fractions_note": "prefill_frac = both passes' prefill flops / their event-timed spans / "
+                          "2.5 PFLOP/s; decode_frac = unique decode bytes / the decode calls' "
+                          "spans / 8 TB/s; the spans overlap (two streams), so each is below "
+                          "what its kernels reach alone; value combines both floors",
         "launch": "per layer pass one decode-rows call and one prefill-rows call; the decode "
                   "calls on a second stream beside the prefill calls (prefill and decode "
                   "times above are each call's own event-timed span, overlapping)",
@@ -686,6 +837,15 @@ def main():
                            "launch_ms": round(alone_ms, 4), "achieved": round(achieved_alone, 2),
                            "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                            "frac": round(achieved_alone / (PEAK_BF16_FLOPS / 1e12), 4)},
+        "clock": None if sclk_mhz is None else {
+            "shader_clock_mhz_under_mfma_load": round(sclk_mhz, 1),
+            "probe": "own back-to-back v_mfma_f32_32x32x16_bf16 loop on every CU right after "
+                     "the timed region (s_memtime against the 100 MHz s_memrealtime)",
+            "probe_tflops": round(probe_tflops, 1),
+            "roofline_frac_at_that_clock": round(
+                achieved / (PEAK_BF16_FLOPS / 1e12 * sclk_mhz / 2400.0), 4),
+            "roofline_alone_frac_at_that_clock": round(
+                achieved_alone / (PEAK_BF16_FLOPS / 1e12 * sclk_mhz / 2400.0), 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -21,7 +21,7 @@ ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_BLOCK_SIZE, ATTN_ERR_GQA = 0, 1
 ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_METADATA, ATTN_ERR_HIP = 5, 6, 7, 8
 ATTN_BF16, ATTN_F32 = 0, 1
 
-EXPORTED = ("attn_workspace_bytes", "attn_varlen_fwd", "attn_check_metadata_host",
+EXPORTED = ("attn_workspace_bytes", "attn_decode_partition_tokens", "attn_varlen_fwd", "attn_check_metadata_host",
             "attn_cascade_workspace_bytes", "attn_cascade_fwd", "attn_check_cascade_host",
             "attn_kv_cache_write", "attn_check_slot_mapping_host", "attn_kv_cache_write_fp8",
             "attn_fp8_decode_fwd", "attn_schedule_bytes", "attn_build_schedule",
@@ -58,6 +58,8 @@ def lib():
         P = ctypes.POINTER
         L.attn_workspace_bytes.argtypes = [P(attn_desc), P(sz)]
         L.attn_workspace_bytes.restype = i32
+        L.attn_decode_partition_tokens.argtypes = [P(attn_desc), P(i32)]
+        L.attn_decode_partition_tokens.restype = i32
         L.attn_varlen_fwd.argtypes = [P(attn_desc), vp, vp, vp, vp, vp, f32, i32, i32, vp, vp,
                                       vp, sz, vp]
         L.attn_varlen_fwd.restype = i32
@@ -112,6 +114,15 @@ def attn_workspace_bytes(desc: attn_desc) -> int:
     st = lib().attn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n))
     if st != ATTN_OK:
         raise AttnError(st, "attn_workspace_bytes")
+    return int(n.value)
+
+
+def attn_decode_partition_tokens(desc: attn_desc) -> int:
+    """The split-KV partition length (keys) the library uses for desc's decode rows."""
+    n = ctypes.c_int32(0)
+    st = lib().attn_decode_partition_tokens(ctypes.byref(desc), ctypes.byref(n))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_partition_tokens")
     return int(n.value)
 
 
@@ -185,6 +196,25 @@ def _check_call(where, desc, q, kv_cache, block_table, query_start_loc, seq_lens
     if tuple(kv_cache.shape) != (2, desc.num_blocks, desc.block_size, desc.num_kv_heads,
                                  desc.head_size):
         raise ValueError("kv_cache shape does not match desc")
+    _check_meta_shapes(desc, block_table, query_start_loc, seq_lens, lse)
+
+
+def _check_meta_shapes(desc, block_table, query_start_loc, seq_lens, lse):
+    """The kernels index these arrays from the descriptor's sizes without bounds checks, so
+    an undersized one would be read or written past its end on the device: refuse it here,
+    before anything is queued."""
+    if tuple(block_table.shape) != (desc.num_seqs, desc.max_blocks_per_seq):
+        raise ValueError(f"block_table must be [num_seqs={desc.num_seqs}, max_blocks_per_seq="
+                         f"{desc.max_blocks_per_seq}], got {tuple(block_table.shape)}")
+    if query_start_loc.dim() != 1 or query_start_loc.numel() != desc.num_seqs + 1:
+        raise ValueError(f"query_start_loc must hold num_seqs + 1 = {desc.num_seqs + 1} "
+                         f"entries, got shape {tuple(query_start_loc.shape)}")
+    if seq_lens.dim() != 1 or seq_lens.numel() != desc.num_seqs:
+        raise ValueError(f"seq_lens must hold num_seqs = {desc.num_seqs} entries, got shape "
+                         f"{tuple(seq_lens.shape)}")
+    if lse is not None and tuple(lse.shape) != (desc.num_tokens, desc.num_heads):
+        raise ValueError(f"lse must be [num_tokens={desc.num_tokens}, num_heads="
+                         f"{desc.num_heads}], got {tuple(lse.shape)}")
 
 
 def attn_cascade_workspace_bytes(desc: attn_desc, common_prefix_len: int) -> int:
@@ -290,6 +320,8 @@ def attn_kv_cache_write_fp8(desc: attn_desc, key, value, slot_mapping, k_scale: 
         raise ValueError("attn_kv_cache_write_fp8 runs on a GPU device")
     _check_kv_rows(desc, key, value, torch.bfloat16, dev)
     _check_tensor("slot_mapping", slot_mapping, torch.int64, dev)
+    if slot_mapping.numel() != desc.num_tokens:
+        raise ValueError("slot_mapping must hold num_tokens entries")
     _fp8_cache_ok(kv_cache, desc, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
@@ -321,6 +353,7 @@ def attn_fp8_decode_fwd(desc: attn_desc, q, kv_cache, block_table, query_start_l
     if tuple(q.shape) != (desc.num_tokens, desc.num_heads, desc.head_size) or \
             tuple(out.shape) != tuple(q.shape):
         raise ValueError("q/out shape does not match desc")
+    _check_meta_shapes(desc, block_table, query_start_loc, seq_lens, lse)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     ws_bytes = 0 if workspace is None else workspace.numel()
@@ -382,6 +415,8 @@ def attn_build_schedule(desc: attn_desc, query_start_loc, seq_lens, causal: bool
     for n, t in (("query_start_loc", query_start_loc), ("seq_lens", seq_lens),
                  ("schedule", schedule)):
         _check_tensor(n, t, torch.int32, dev)
+    if query_start_loc.numel() != desc.num_seqs + 1 or seq_lens.numel() != desc.num_seqs:
+        raise ValueError("query_start_loc / seq_lens must hold num_seqs + 1 / num_seqs entries")
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     st = lib().attn_build_schedule(ctypes.byref(desc), _ptr(query_start_loc), _ptr(seq_lens),

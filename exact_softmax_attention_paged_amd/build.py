@@ -1,4 +1,5 @@
-"""Compile the gfx950 HIP sources of this package into libattn.so (in the package folder).
+"""Compile the gfx950 HIP sources of this package into libattn.so, and the device-ceiling
+probes (csrc/probes.hip, measurement only) into libattn_probes.so, both in the package folder.
 
 Run ``python -m exact_softmax_attention_paged_amd.build`` or call ``build()``.
 """
@@ -16,6 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = ["attn_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip",
            "cascade_bf16.hip", "kv_write.hip", "schedule.hip"]
+PROBES_LIB = os.path.join(PKG, "libattn_probes.so")
+PROBES_SOURCES = ["probes.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the device code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -31,10 +34,15 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Always recompiles; writes the library atomically and returns its path."""
-    tmp = LIB + ".tmp"
+    """Always recompiles both libraries (each written atomically); returns libattn.so's path."""
+    _compile(PROBES_SOURCES, PROBES_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
+
+
+def _compile(sources, lib, verbose: bool) -> str:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,8 +52,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msg}")
     if verbose and msg.strip():
         print(msg)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -208,6 +208,14 @@ attn_status attn_workspace_bytes(const attn_desc* desc, size_t* bytes) {
   return ATTN_OK;
 }
 
+attn_status attn_decode_partition_tokens(const attn_desc* desc, int32_t* tokens) {
+  if (tokens == nullptr) return ATTN_ERR_NULL;
+  const attn_status s = check_desc(desc);
+  if (s != ATTN_OK) return s;
+  *tokens = partition_tokens(desc);
+  return ATTN_OK;
+}
+
 attn_status attn_varlen_fwd(const attn_desc* desc, const void* q, const void* kv_cache,
                             const int32_t* block_table, const int32_t* query_start_loc,
                             const int32_t* seq_lens, float scale, int32_t causal,

@@ -102,6 +102,14 @@ typedef struct attn_desc {
 attn_status attn_workspace_bytes(const attn_desc* desc, size_t* bytes);
 
 /*
+ * attn_decode_partition_tokens: the split-KV partition length (keys) that attn_varlen_fwd uses
+ * for the decode rows of `desc`: desc->partition_tokens when it is set, else the library's
+ * choice described at attn_desc.partition_tokens. A host-side query; nothing touches the GPU.
+ * Errors: ATTN_ERR_NULL (desc or tokens NULL) and the descriptor errors of attn_workspace_bytes.
+ */
+attn_status attn_decode_partition_tokens(const attn_desc* desc, int32_t* tokens);
+
+/*
  * attn_varlen_fwd: exact attention for a variable-length batch over a paged KV cache.
  *
  * For request r, let q0 = query_start_loc[r], ql = query_start_loc[r+1] - q0,

@@ -22,6 +22,17 @@ def test_header_declares_the_python_names():
     assert _declared() == sorted(A.EXPORTED)
 
 
+def test_probe_library_exports_its_header():
+    src = open(os.path.join(ROOT, "include", "attn_probes.h")).read()
+    declared = sorted(set(re.findall(r"^\S[^\n(]*?\b(attn_probe_[a-z0-9_]+)\s*\(", src, re.M)))
+    assert declared == ["attn_probe_mfma_loop", "attn_probe_read_stream"]
+    lib = os.path.join(os.path.dirname(A.LIB_PATH), "libattn_probes.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (attn_probe_\w+)", out))
+    assert set(declared) <= exported
+
+
 def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -345,3 +356,22 @@ def test_default_partition_follows_the_batch_size():
     # 64 q heads on one kv head form 4 workgroups of 16 heads: 64 x 4 = 256 per partition,
     # so 1024-key partitions (8 of them) are the longest reaching 2048
     assert need(64, 8192, heads=64, kv=1) == expected(64, 8, heads=64)
+
+
+def test_partition_query_reports_the_length_in_use():
+    def part(num_decodes, max_seq_len, pt=0, heads=32, kv=8):
+        return A.attn_decode_partition_tokens(_desc(
+            num_seqs=num_decodes, num_tokens=num_decodes, num_decodes=num_decodes,
+            max_query_len=1, max_seq_len=max_seq_len, num_heads=heads, num_kv_heads=kv,
+            num_blocks=num_decodes * 3000, max_blocks_per_seq=-(-max_seq_len // 16),
+            partition_tokens=pt))
+    assert part(256, 8192) == 16384
+    assert part(120, 32768) == 8192
+    assert part(1, 40000) == 256
+    assert part(64, 8192, heads=64, kv=1) == 1024
+    assert part(256, 8192, pt=512) == 512
+    n = ctypes.c_int32(0)
+    assert A.lib().attn_decode_partition_tokens(ctypes.byref(_desc(block_size=24)),
+                                                ctypes.byref(n)) == A.ATTN_ERR_BLOCK_SIZE
+    assert A.lib().attn_decode_partition_tokens(ctypes.byref(_desc()), None) == A.ATTN_ERR_NULL
+
