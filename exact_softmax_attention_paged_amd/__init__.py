@@ -25,7 +25,9 @@ EXPORTED = ("attn_workspace_bytes", "attn_decode_partition_tokens", "attn_varlen
             "attn_cascade_workspace_bytes", "attn_cascade_fwd", "attn_check_cascade_host",
             "attn_kv_cache_write", "attn_check_slot_mapping_host", "attn_kv_cache_write_fp8",
             "attn_fp8_decode_fwd", "attn_schedule_bytes", "attn_build_schedule",
-            "attn_varlen_fwd_scheduled", "attn_status_str")
+            "attn_varlen_fwd_scheduled", "attn_varlen_fwd_noalloc", "attn_status_str")
+# bytes of the library's fixed device array used by attn_varlen_fwd_noalloc
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 
 
 class attn_desc(ctypes.Structure):
@@ -63,6 +65,9 @@ def lib():
         L.attn_varlen_fwd.argtypes = [P(attn_desc), vp, vp, vp, vp, vp, f32, i32, i32, vp, vp,
                                       vp, sz, vp]
         L.attn_varlen_fwd.restype = i32
+        L.attn_varlen_fwd_noalloc.argtypes = [P(attn_desc), vp, vp, vp, vp, vp, f32, i32, i32,
+                                              vp, vp, vp]
+        L.attn_varlen_fwd_noalloc.restype = i32
         L.attn_check_metadata_host.argtypes = [P(attn_desc), vp, vp, vp]
         L.attn_check_metadata_host.restype = i32
         L.attn_cascade_workspace_bytes.argtypes = [P(attn_desc), i32, P(sz)]
@@ -172,6 +177,26 @@ def attn_varlen_fwd(desc: attn_desc, q, kv_cache, block_table, query_start_loc, 
                                _ptr(workspace), ws_bytes, ctypes.c_void_p(stream.cuda_stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_varlen_fwd")
+
+
+def attn_varlen_fwd_noalloc(desc: attn_desc, q, kv_cache, block_table, query_start_loc,
+                            seq_lens, scale: float, causal: bool, window: int, out, lse,
+                            stream=None) -> None:
+    """attn_varlen_fwd without a workspace argument: the decode rows' partial results go to the
+    library's fixed device array (NOALLOC_SCRATCH_BYTES per GPU), so the call allocates
+    nothing. Calls that could overlap on one GPU race on that array and must not be issued."""
+    import torch
+    _check_call("attn_varlen_fwd_noalloc", desc, q, kv_cache, block_table, query_start_loc,
+                seq_lens, out, lse, None)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = lib().attn_varlen_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(kv_cache),
+                                       _ptr(block_table), _ptr(query_start_loc),
+                                       _ptr(seq_lens), float(scale), 1 if causal else 0,
+                                       int(window), _ptr(out), _ptr(lse),
+                                       ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_varlen_fwd_noalloc")
 
 
 def _check_call(where, desc, q, kv_cache, block_table, query_start_loc, seq_lens, out, lse,

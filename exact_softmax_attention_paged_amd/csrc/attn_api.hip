@@ -6,11 +6,38 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "kernels.hpp"
 
 namespace {
+
+// Device memory of attn_varlen_fwd_noalloc: the split-KV partial results and the decode
+// schedule, in a fixed array that every GPU the library runs on holds until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol): its device address is looked up once per device with hipGetSymbolAddress, and
+// that address is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+attn_status scratch_address(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return ATTN_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
 
 // Split-KV partition length when the descriptor leaves it at 0: the longest of 16384, 8192,
 // ..., 256 keys that still gives the split kernel at least 2048 workgroups (counted from
@@ -255,6 +282,33 @@ attn_status attn_varlen_fwd(const attn_desc* desc, const void* q, const void* kv
     if (attn::launch_prefill_bf16(pp, st) != hipSuccess) return ATTN_ERR_HIP;
   }
   return ATTN_OK;
+}
+
+attn_status attn_varlen_fwd_noalloc(const attn_desc* desc, const void* q, const void* kv_cache,
+                                    const int32_t* block_table,
+                                    const int32_t* query_start_loc, const int32_t* seq_lens,
+                                    float scale, int32_t causal, int32_t window, void* out,
+                                    float* lse, void* stream) {
+  const attn_status s = check_desc(desc);
+  if (s != ATTN_OK) return s;
+  // the same checks attn_varlen_fwd makes, before the workspace size is looked at
+  if (window > 0 && !causal) return ATTN_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (desc->num_seqs == 0 || desc->num_tokens == 0) return ATTN_OK;
+  if (q == nullptr || kv_cache == nullptr || block_table == nullptr ||
+      query_start_loc == nullptr || seq_lens == nullptr || out == nullptr)
+    return ATTN_ERR_NULL;
+  const size_t need = workspace_for(desc, decode_max_parts(desc, window));
+  if (need > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    const attn_status a = scratch_address(&ws);
+    if (a != ATTN_OK) return a;
+  }
+  return attn_varlen_fwd(desc, q, kv_cache, block_table, query_start_loc, seq_lens, scale,
+                         causal, window, out, lse, ws, need > 0 ? (size_t)ATTN_NOALLOC_SCRATCH_BYTES
+                                                                : 0,
+                         stream);
 }
 
 attn_status attn_cascade_workspace_bytes(const attn_desc* desc, int32_t common_prefix_len,

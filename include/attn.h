@@ -25,7 +25,8 @@
  * Conventions for every entry point:
  *   - All tensors are caller-owned. Device pointers must stay valid until the work queued
  *     on `stream` has finished. The library never allocates, frees or synchronises device
- *     memory and keeps no global state; calls are thread-safe.
+ *     memory and keeps no global state (except the fixed device array of
+ *     attn_varlen_fwd_noalloc); calls are thread-safe.
  *   - Errors are reported as attn_status codes. Argument errors are detected on the host
  *     before anything is queued, so a failed call leaves every buffer untouched.
  *   - Device-side metadata (block_table, query_start_loc, seq_lens) is trusted by
@@ -155,6 +156,32 @@ attn_status attn_varlen_fwd(const attn_desc* desc, const void* q, const void* kv
                             const int32_t* seq_lens, float scale, int32_t causal,
                             int32_t window, void* out, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * attn_varlen_fwd_noalloc: attn_varlen_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation). It
+ * takes no workspace: the decode rows' partial results and work schedule go to a fixed device
+ * array of ATTN_NOALLOC_SCRATCH_BYTES bytes inside the library, of which every GPU the library
+ * runs on holds one copy until the process ends (its address is looked up on the first call
+ * on each device, with that device current; the caller's current device must be the one its
+ * stream and tensors live on). The call allocates and frees nothing and runs the same kernels
+ * as attn_varlen_fwd, so its results are identical.
+ *
+ * Every call on one GPU shares that GPU's array: calls that may overlap on one GPU (on
+ * different streams, or from different threads without ordering) race on it and must not be
+ * issued. Nothing in the array needs to start at zero; it keeps whatever the last call left.
+ *
+ * Arguments and errors: those of attn_varlen_fwd without workspace / workspace_bytes, plus
+ * ATTN_ERR_WORKSPACE when the call would need more than ATTN_NOALLOC_SCRATCH_BYTES (i.e. when
+ * attn_workspace_bytes, with the window's partition cap, exceeds it), and ATTN_ERR_HIP when the
+ * array's device address cannot be obtained.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+attn_status attn_varlen_fwd_noalloc(const attn_desc* desc, const void* q, const void* kv_cache,
+                                    const int32_t* block_table,
+                                    const int32_t* query_start_loc, const int32_t* seq_lens,
+                                    float scale, int32_t causal, int32_t window, void* out,
+                                    float* lse, void* stream);
 
 /*
  * attn_check_metadata_host: validates host copies of the metadata against desc:

@@ -375,3 +375,35 @@ def test_partition_query_reports_the_length_in_use():
                                                 ctypes.byref(n)) == A.ATTN_ERR_BLOCK_SIZE
     assert A.lib().attn_decode_partition_tokens(ctypes.byref(_desc()), None) == A.ATTN_ERR_NULL
 
+
+# ---------------------------------------------------------------- no-allocation entry point
+def _noalloc(desc, causal=1, window=0, scale=0.125, q=FAKE, out=FAKE):
+    return A.lib().attn_varlen_fwd_noalloc(ctypes.byref(desc), q, FAKE, FAKE, FAKE, FAKE, scale,
+                                           causal, window, out, None, None)
+
+
+def test_noalloc_limit_matches_the_header():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u \* (\d+)u \* (\d+)u\)", src)
+    assert m and int(m[1]) * int(m[2]) * int(m[3]) == A.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_argument_errors_and_size_limit():
+    """Argument errors as for attn_varlen_fwd; a call whose split-KV partial results would not
+    fit the fixed array is refused with ATTN_ERR_WORKSPACE before anything touches a GPU."""
+    assert _noalloc(_desc(block_size=24)) == A.ATTN_ERR_BLOCK_SIZE
+    assert _noalloc(_desc(), causal=0, window=8) == A.ATTN_ERR_UNSUPPORTED
+    assert _noalloc(_desc(), scale=0.0) == A.ATTN_ERR_UNSUPPORTED
+    assert A.lib().attn_varlen_fwd_noalloc(None, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 1, 0, FAKE,
+                                           None, None) == A.ATTN_ERR_NULL
+    # 1024 decode requests of 32768 keys in 128-key partitions, 8 q heads: 1024 * 8 * 256
+    # partials of 129 floats = 270 MB > 128 MiB
+    big = _desc(num_seqs=1024, num_tokens=1024, num_decodes=1024, max_query_len=1,
+                max_seq_len=32768, max_blocks_per_seq=2048, partition_tokens=128)
+    assert A.attn_workspace_bytes(big) > A.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(big) == A.ATTN_ERR_WORKSPACE
+    # with a 256-key window the same batch needs only 3 partitions per request: it fits, and
+    # the call then fails on the NULL q instead
+    assert _noalloc(big, window=256, q=None) == A.ATTN_ERR_NULL
+    empty = _desc(num_seqs=0, num_tokens=0, num_decodes=0, max_query_len=0, max_seq_len=0)
+    assert _noalloc(empty, q=None, out=None) == A.ATTN_OK
