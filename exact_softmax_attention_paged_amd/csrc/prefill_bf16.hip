@@ -120,12 +120,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   constexpr int TPR = D / 8;          // lanes per row in a direct load (16 bytes each)
   constexpr int RPI = kWave / TPR;    // rows per direct-load instruction (4 or 8: divides 16)
   constexpr int NI = kBC / RPI;       // instructions per K (or V) tile
-  // Waves 0-3 (one of the two waves on each SIMD) issue all direct loads of a tile. A wave
-  // stalls at issue while the vector-memory queue is full; with the loads on one wave of each
-  // pair, the other one keeps the MFMA unit busy meanwhile (measured 2-3 % faster on gfx950
-  // than spreading the loads over all 8 waves).
-  constexpr int kDmaWaves = kWaves / 2;
-  constexpr int IPW = NI / kDmaWaves;   // of them issued by each such wave
+  // Every wave issues NI / 8 of a tile's direct loads (each a K and a V instruction), one after
+  // every other k-chunk of its QK^T MFMAs: a wave stalls at issue while the CU's vector-memory
+  // queue is full, so the loads of a whole tile issued in one burst held the issuing waves for
+  // most of a thousand cycles per tile (s_memtime stamps on gfx950).
+  constexpr int kDmaWaves = kWaves;
+  constexpr int IPW = NI / kDmaWaves;   // of them issued by each wave
   constexpr int TILEB = kBC * ROWB;   // bytes of one K (or V) tile
   static_assert(IPW * kDmaWaves == NI, "tile rows must split evenly over the waves");
 
@@ -173,7 +173,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave index, uniform
   const int lane = tid % kWave;
   const int dw = w % kDmaWaves;                     // direct-load slot of this wave
-  const bool dma_wave = w < kDmaWaves;
   const int32_t* __restrict__ bt = p.block_table + (int64_t)r * p.max_blocks + p.kv_skip_blocks;
   // Block ids of this wave's direct loads of tile 0, loaded beside the sequence metadata
   // (they depend on the request only), so that the first tile's loads wait for one memory
@@ -182,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   // the block-table row and to the rows of this launch's requests, so the load is always in
   // bounds, and it is unconditional so that it is issued before the metadata is waited for.
   const int row_blocks = p.max_blocks - p.kv_skip_blocks;   // entries left in the row
-  int32_t ids0;
+  int32_t ids0, ids0_row_in_block;
   {
     const int u = min(lane, IPW - 1);
     const uint32_t grp = (uint32_t)(((dw + kDmaWaves * u) * RPI) >> 4);
@@ -190,6 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
     const int64_t idx = min((int64_t)r * p.max_blocks + p.kv_skip_blocks + max(bi, 0),
                             (int64_t)(p.seq_begin + p.num_seqs) * p.max_blocks - 1);
     ids0 = p.block_table[idx];
+    ids0_row_in_block = (int)grp * 16 - bi * p.block_size;
   }
   // The request's metadata (in the prefix pass r is 0, so these loads are valid there too):
   // three scalar loads and one wait for them, after the vector load above has been issued,
@@ -255,17 +255,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   // ---- K/V tiles go from HBM straight into LDS (global_load_lds_dwordx4: lane l of one
   // instruction lands at LDS base + 16 l), so there is no register staging and no LDS store.
   // An instruction covers RPI consecutive rows; they lie in one 16-key group, which lies in
-  // one cache block (block_size is a multiple of 16), so each instruction needs one block id
-  // (block index of group g: g / (block_size / 16), from the host's 32.32 reciprocal). The
-  // ids of a tile are loaded one tile ahead, lane u holding that of the wave's instruction u,
-  // and read back with v_readlane, so the address arithmetic is scalar. Rows past seq_len
-  // load row seq_len - 1: its scores are masked and 0 * (finite V) adds nothing, so no
-  // zeroing is needed. Because the destination of a lane is fixed, the row layout is
-  // permuted on the source side: LDS chunk slot p of row r holds d-chunk p ^ swz(r), which
-  // keeps both MFMA operand reads free of bank conflicts.
-  const uint32_t block_elems = (uint32_t)(p.block_size * p.num_kv_heads * D);   // < 2^31
+  // one cache block (block_size is a multiple of 16). The block ids of the groups of a tile's
+  // instructions are loaded one tile ahead (lane u holds that of the wave's instruction u) and
+  // turned into the cache row index of each group's first key (block * block_size + the
+  // group's offset in its block); an instruction's address is then one multiply-add of that
+  // row index (read back with v_readlane) with a per-lane base, which keeps the scalar unit
+  // (shared by the CU's four SIMDs) nearly free of address arithmetic. Rows past seq_len load
+  // row seq_len - 1: its scores are masked and 0 * (finite V) adds nothing, so no zeroing is
+  // needed. Because the destination of a lane is fixed, the row layout is permuted on the
+  // source side: LDS chunk slot p of row r holds d-chunk p ^ swz(r), which keeps both MFMA
+  // operand reads free of bank conflicts.
   const int kv_row = p.num_kv_heads * D;
-  const int groups_per_block = p.block_size / 16;
+  const uint32_t row_bytes = (uint32_t)(kv_row * 2);
   const int last_group = (sl - 1) >> 4;
   const int l_row = lane / TPR;                      // row of this lane within an instruction
   const int l_slot = lane % TPR;                     // LDS chunk slot of this lane
@@ -276,49 +277,47 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   auto block_index = [&](int grp) {
     return (uint32_t)(((uint64_t)(uint32_t)grp * p.group_recip) >> 32);
   };
-  // block ids of a tile's IPW instructions: lane u (u < IPW) loads the id of instruction u
-  auto fetch_ids = [&](int tile) {
-    const int u = min(lane, IPW - 1);
-    return bt[block_index(group_of(tile, u))];
+  // Groups of a tile's IPW instructions (lane u < IPW: instruction u; group_of clamps to the
+  // last group, so every index is a valid entry of the request's row): fetch_ids loads their
+  // block ids and keeps each group's offset in its block; row_base, once the load has landed,
+  // gives the cache row index of each group's first key.
+  struct Ids {
+    int32_t blk;
+    int32_t row_in_block;
   };
-  // Lane part of the source offset (elements) for tiles that lie wholly below seq_len: row
-  // l_row of the instruction, d-chunk l_slot ^ swizzle(row). The swizzle depends on the row
-  // modulo 16, which is the same for every instruction of this wave (j RPI = dw RPI mod 16).
-  const uint32_t lane_src =
-      (uint32_t)(l_row * kv_row + 8 * (l_slot ^ swizzle<D>(dw * RPI + l_row)));
-  const uint32_t head_off = (uint32_t)(kvh * D);
-  auto issue_tile = [&](int tile_in, int buf, int32_t ids) {
-    if (!dma_wave) return;
-    // the tile index is wave-uniform; saying so keeps the address arithmetic scalar
+  auto fetch_ids = [&](int tile) {
+    const int grp = group_of(tile, min(lane, IPW - 1));
+    const uint32_t bidx = block_index(grp);
+    return Ids{bt[bidx], grp * 16 - (int)bidx * p.block_size};
+  };
+  auto row_base = [&](const Ids& ids) {
+    return (uint32_t)ids.blk * (uint32_t)p.block_size + (uint32_t)ids.row_in_block;
+  };
+  // Per-lane byte part of the source addresses: kv head and d-chunk l_slot ^ swizzle(row) (the
+  // swizzle depends on the row modulo 16 only, which is the same for every instruction of this
+  // wave: j RPI = dw RPI mod 16).
+  const uint32_t chunk_bytes =
+      (uint32_t)(kvh * D * 2 + 16 * (l_slot ^ swizzle<D>(dw * RPI + l_row)));
+  const unsigned char* const k_lane = reinterpret_cast<const unsigned char*>(kcache) + chunk_bytes;
+  const unsigned char* const v_lane = reinterpret_cast<const unsigned char*>(vcache) + chunk_bytes;
+  // the K and V direct loads of this wave's instruction u of a tile into buffer buf; rb holds
+  // the row bases of the tile's groups. The lane's key is clamped to seq_len - 1 (a no-op for
+  // tiles wholly below seq_len), so the same arithmetic serves full and tail tiles.
+  auto issue_one = [&](int tile, int buf, uint32_t rb, int u) {
+    const int j = dw + kDmaWaves * u;                // instruction index within the tile
+    const uint32_t rbu = __builtin_amdgcn_readlane(rb, u);
+    const int key = min(tile * kBC + j * RPI + l_row, sl - 1);
+    const uint32_t row = rbu + (uint32_t)(key - group_of(tile, u) * 16);
+    const uint32_t lds_k = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(sKV + buf * (2 * TILEB) + j * (RPI * ROWB)));
+    dma_b128(k_lane + (uint64_t)row * row_bytes, lds_k);
+    dma_b128(v_lane + (uint64_t)row * row_bytes, lds_k + TILEB);
+  };
+  auto issue_tile = [&](int tile_in, int buf, uint32_t rb) {
+    // the tile index is wave-uniform; saying so keeps its arithmetic scalar
     const int tile = __builtin_amdgcn_readfirstlane(tile_in);
-    unsigned char* const dst = sKV + buf * (2 * TILEB);
-    const bool full = tile * kBC + kBC <= sl;        // wave-uniform
 #pragma unroll
-    for (int u = 0; u < IPW; ++u) {
-      const int j = dw + kDmaWaves * u;              // instruction index within the tile
-      const int32_t blk = __builtin_amdgcn_readlane(ids, u);
-      uint64_t off;
-      if (full) {
-        // rows first .. first + RPI - 1 all lie in the block of group first / 16
-        const int first = tile * kBC + j * RPI;
-        const uint32_t bidx = block_index(first >> 4);
-        off = (uint64_t)(uint32_t)blk * block_elems +
-              (uint32_t)((first - (int)bidx * p.block_size) * kv_row) + head_off + lane_src;
-      } else {
-        // tail tile: rows past seq_len load row seq_len - 1 (its group is the last group)
-        const int grp = __builtin_amdgcn_readfirstlane(group_of(tile, u));
-        const uint32_t bidx = block_index(grp);
-        const int row = j * RPI + l_row;
-        const int key = min(tile * kBC + row, sl - 1);
-        const int slot = (grp - (int)bidx * groups_per_block) * 16 + (key - grp * 16);
-        off = (uint64_t)(uint32_t)blk * block_elems +
-              (uint32_t)(slot * kv_row + head_off + 8 * (l_slot ^ swizzle<D>(row)));
-      }
-      const uint32_t lds_k = __builtin_amdgcn_readfirstlane(
-          (uint32_t)(uintptr_t)(dst + j * (RPI * ROWB)));
-      dma_b128(kcache + off, lds_k);
-      dma_b128(vcache + off, lds_k + TILEB);
-    }
+    for (int u = 0; u < IPW; ++u) issue_one(tile, buf, rb, u);
   };
 
   // per-lane byte offsets of the transposing V reads within a tile for (kt, g) = (0, 0):
@@ -367,12 +366,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
     }
   }
 
-  int32_t ids = 0;
+  Ids ids{0, 0};
   if (t_begin < t_end) {
-    int32_t first_ids;
-    if (t_begin == 0 && kBC <= sl && row_blocks > 0) first_ids = ids0;
+    Ids first_ids;
+    if (t_begin == 0 && kBC <= sl && row_blocks > 0) first_ids = Ids{ids0, ids0_row_in_block};
     else first_ids = fetch_ids(t_begin);
-    issue_tile(t_begin, 0, first_ids);
+    issue_tile(t_begin, 0, row_base(first_ids));
     ids = fetch_ids(t_begin + 1);      // clamped to the last group: always a valid entry
   }
   wait_vmem();                         // Q, tile t_begin and the ids of tile t_begin + 1
@@ -380,12 +379,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   int buf = 0;
   for (int t = t_begin; t < t_end; ++t) {
     // tile t + 1 goes to the other buffer, which every wave finished reading (tile t - 1)
-    // before the barrier that ended the previous iteration
-    const bool more = t + 1 < t_end;
-    if (more) {
-      issue_tile(t + 1, buf ^ 1, ids);
-      ids = fetch_ids(t + 2);
-    }
+    // before the barrier that ended the previous iteration. Its loads are issued whether or
+    // not a tile t + 1 exists (past the last tile they reload the last rows into a buffer no
+    // one reads again), which keeps them free of branches between the QK^T MFMAs.
+    const uint32_t rb_next = row_base(ids);
+    const int t_next = __builtin_amdgcn_readfirstlane(t + 1);
+    ids = fetch_ids(t + 2);
 
     const int kb = t * kBC;
     if (wave_active && kb < w_kv_hi && kb + kBC > w_kv_lo) {
@@ -401,6 +400,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
         // K row kt*32 + lq has the swizzle of row lq (it depends on the row modulo 16)
         const int ks = swizzle<D>(lq);
         const unsigned char* kp = tK + lq * ROWB;
+        constexpr int kGap = KC / IPW;               // chunks between this wave's loads
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
           const int off = 16 * ((2 * c + h) ^ ks);
@@ -408,6 +408,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
           for (int kt = 0; kt < kKT; ++kt)
             sc[kt] = mfma32x32x16(
                 *reinterpret_cast<const bf16x8*>(kp + kt * 32 * ROWB + off), qf[c], sc[kt]);
+          if (c % kGap == 0) issue_one(t_next, buf ^ 1, rb_next, c / kGap);
         }
         // software pipeline: the K operands of chunk c + 1 are read while chunk c multiplies
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * kKT, 0);   // LDS reads
@@ -513,6 +514,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
             o[dc] = mfma32x32x16(va, pb, o[dc]);
           }
         }
+    } else {
+      issue_tile(t_next, buf ^ 1, rb_next);         // a wave with nothing to compute here
     }
     wait_vmem();        // this wave's part of tile t + 1 is in LDS ...
     barrier_kv();       // ... and everyone's, and nobody reads tile t any more
