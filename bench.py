@@ -429,7 +429,8 @@ def configs_report(dev, seed):
     """Every workload (the tiny fp32 case, the BERT-large-shaped encoder, the GPT-2-shaped
     varlen prefill, the paged GQA decode, the mixed long-context batch) through one plain
     attn_varlen_fwd call per layer pass, with the library's default decode partition, and the
-    paged GQA decode again at its stated 512-token partitions. One JSON line per (workload,
+    paged GQA decode again at its stated 512-token partitions (each decode-only line also
+    times attn_varlen_fwd_prescheduled with the decode schedule built ahead, and the build). One JSON line per (workload,
     pass, partition): mean call time by HIP events with the inputs hot in the caches, the
     algorithmic prefill TFLOP/s and decode GB/s of that call, and its % of the MI355X roofline,
     (prefill flops / MFMA peak + decode bytes / 8 TB/s) / call time, the MFMA peak being fp32
@@ -472,6 +473,19 @@ def configs_report(dev, seed):
                        if b.num_decodes else None,
                        "call_ms": round(t, 4), "prefill_gflop": round(flops / 1e9, 3)}
                 rec.update(_rates(t, flops, dec_unique if b.num_decodes else 0, peak))
+                if b.num_decodes == b.num_seqs:
+                    # the decode schedule built once ahead (a batch builds it once for all
+                    # its layers) and the call that reads it instead of building its own
+                    ds = torch.empty(A.attn_decode_schedule_bytes(desc, window) // 4,
+                                     dtype=torch.int32, device=dev)
+                    tb = _time_ms(lambda: A.attn_build_decode_schedule(desc, sl, window, ds),
+                                  reps)
+                    tp = _time_ms(lambda: A.attn_varlen_fwd_prescheduled(
+                        desc, q, kv, bt, qsl, sl, b.scale, causal, window, out, lse, ws,
+                        decode_schedule=ds), reps)
+                    pre = {"call_ms": round(tp, 4), "schedule_build_ms": round(tb, 4)}
+                    pre.update(_rates(tp, 0, dec_unique, peak))
+                    rec["prescheduled"] = pre
                 if k <= 3:
                     rec["cold"] = _cold_rates(A, b, desc, k, li, causal, window, bt, qsl, sl,
                                               ws, flops, peak, dev)

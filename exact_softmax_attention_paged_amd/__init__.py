@@ -25,7 +25,9 @@ EXPORTED = ("attn_workspace_bytes", "attn_decode_partition_tokens", "attn_varlen
             "attn_cascade_workspace_bytes", "attn_cascade_fwd", "attn_check_cascade_host",
             "attn_kv_cache_write", "attn_check_slot_mapping_host", "attn_kv_cache_write_fp8",
             "attn_fp8_decode_fwd", "attn_schedule_bytes", "attn_build_schedule",
-            "attn_varlen_fwd_scheduled", "attn_varlen_fwd_noalloc", "attn_status_str")
+            "attn_varlen_fwd_scheduled", "attn_decode_schedule_bytes",
+            "attn_build_decode_schedule", "attn_varlen_fwd_prescheduled",
+            "attn_varlen_fwd_noalloc", "attn_status_str")
 # bytes of the library's fixed device array used by attn_varlen_fwd_noalloc
 NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 
@@ -93,6 +95,13 @@ def lib():
         L.attn_varlen_fwd_scheduled.argtypes = [P(attn_desc), vp, vp, vp, vp, vp, f32, i32, i32,
                                                 vp, vp, vp, sz, vp, sz, vp]
         L.attn_varlen_fwd_scheduled.restype = i32
+        L.attn_decode_schedule_bytes.argtypes = [P(attn_desc), i32, P(sz)]
+        L.attn_decode_schedule_bytes.restype = i32
+        L.attn_build_decode_schedule.argtypes = [P(attn_desc), vp, i32, vp, sz, vp]
+        L.attn_build_decode_schedule.restype = i32
+        L.attn_varlen_fwd_prescheduled.argtypes = [P(attn_desc), vp, vp, vp, vp, vp, f32, i32,
+                                                   i32, vp, vp, vp, sz, vp, sz, vp, sz, vp]
+        L.attn_varlen_fwd_prescheduled.restype = i32
         L.attn_check_slot_mapping_host.argtypes = [P(attn_desc), vp]
         L.attn_check_slot_mapping_host.restype = i32
         L.attn_status_str.argtypes = [i32]
@@ -469,3 +478,57 @@ def attn_varlen_fwd_scheduled(desc: attn_desc, q, kv_cache, block_table, query_s
         ctypes.c_void_p(stream.cuda_stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_varlen_fwd_scheduled")
+
+
+def attn_decode_schedule_bytes(desc: attn_desc, window: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().attn_decode_schedule_bytes(ctypes.byref(desc), int(window), ctypes.byref(n))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_schedule_bytes")
+    return int(n.value)
+
+
+def attn_build_decode_schedule(desc: attn_desc, seq_lens, window: int, schedule,
+                               stream=None) -> None:
+    """Queue the build of the decode work schedule into ``schedule`` (int32 device tensor of
+    at least attn_decode_schedule_bytes(desc, window) / 4 elements)."""
+    import torch
+    dev = schedule.device
+    if dev.type != "cuda":
+        raise ValueError("attn_build_decode_schedule runs on a GPU device")
+    for n, t in (("seq_lens", seq_lens), ("schedule", schedule)):
+        _check_tensor(n, t, torch.int32, dev)
+    if seq_lens.numel() != desc.num_seqs:
+        raise ValueError("seq_lens must hold num_seqs entries")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = lib().attn_build_decode_schedule(ctypes.byref(desc), _ptr(seq_lens), int(window),
+                                          _ptr(schedule), schedule.numel() * 4,
+                                          ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_build_decode_schedule")
+
+
+def attn_varlen_fwd_prescheduled(desc: attn_desc, q, kv_cache, block_table, query_start_loc,
+                                 seq_lens, scale: float, causal: bool, window: int, out, lse,
+                                 workspace, prefill_schedule=None, decode_schedule=None,
+                                 stream=None) -> None:
+    """attn_varlen_fwd that reads the prefill and / or decode work schedule built ahead
+    (either may be None: that part is then scheduled by the call itself)."""
+    import torch
+    _check_call("attn_varlen_fwd_prescheduled", desc, q, kv_cache, block_table,
+                query_start_loc, seq_lens, out, lse, workspace)
+    for n, t in (("prefill_schedule", prefill_schedule), ("decode_schedule", decode_schedule)):
+        _check_tensor(n, t, torch.int32, q.device, allow_none=True)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    ps_bytes = 0 if prefill_schedule is None else prefill_schedule.numel() * 4
+    ds_bytes = 0 if decode_schedule is None else decode_schedule.numel() * 4
+    st = lib().attn_varlen_fwd_prescheduled(
+        ctypes.byref(desc), _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(query_start_loc),
+        _ptr(seq_lens), float(scale), 1 if causal else 0, int(window), _ptr(out), _ptr(lse),
+        _ptr(workspace), ws_bytes, _ptr(prefill_schedule), ps_bytes, _ptr(decode_schedule),
+        ds_bytes, ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_varlen_fwd_prescheduled")

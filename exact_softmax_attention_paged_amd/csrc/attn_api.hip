@@ -104,16 +104,20 @@ int64_t decode_max_parts(const attn_desc* d, int32_t window) {
 }
 
 // Split-KV workspace: the partitions' fp32 results ([num_decodes][Hq][max_parts][d], then
-// [num_decodes][Hq][max_parts] log-sum-exps), then, from a 256-byte boundary, the decode work
-// schedule (one count and one int32 per (request, partition) slot).
+// [num_decodes][Hq][max_parts] log-sum-exps), then, from a 256-byte boundary, the decode
+// schedule region (below).
 int64_t decode_results_bytes(const attn_desc* d, int64_t max_parts) {
   const int64_t rows = (int64_t)d->num_decodes * d->num_heads * max_parts;
   return ceil_div((rows * d->head_size + rows) * 4, 256) * 256;
 }
+// Decode schedule region: the item count, then one int32 per (request, partition) slot.
+int64_t decode_schedule_ints(const attn_desc* d, int64_t max_parts) {
+  return 1 + (int64_t)d->num_decodes * max_parts;
+}
 size_t workspace_for(const attn_desc* d, int64_t max_parts) {
   if (!uses_split_decode(d)) return 0;
-  const int64_t sched = (1 + (int64_t)d->num_decodes * max_parts) * 4;
-  return (size_t)(decode_results_bytes(d, max_parts) + ceil_div(sched, 256) * 256);
+  return (size_t)(decode_results_bytes(d, max_parts) +
+                  ceil_div(decode_schedule_ints(d, max_parts) * 4, 256) * 256);
 }
 
 size_t round256(int64_t bytes) { return (size_t)ceil_div(bytes, 256) * 256; }
@@ -202,6 +206,11 @@ attn::DecodeParams decode_params(const attn_desc& d, const attn::PrefillParams& 
   dp.scale = pp.scale;
   dp.group_recip = pp.group_recip;
   return dp;
+}
+
+// Decode schedule region built ahead of a call, for the window's partition cap.
+size_t decode_schedule_bytes_for(const attn_desc* d, int32_t window) {
+  return round256(decode_schedule_ints(d, decode_max_parts(d, window)) * 4);
 }
 
 // Prefill work schedule: one int32 count plus one int32 per (prefill request, q tile) slot.
@@ -490,6 +499,88 @@ attn_status attn_varlen_fwd_scheduled(const attn_desc* desc, const void* q, cons
     pp.num_seqs = d.num_seqs - d.num_decodes;
     pp.schedule = schedule;
     pp.max_qtiles = (int32_t)schedule_max_qtiles(&d);
+    if (attn::launch_prefill_bf16(pp, st) != hipSuccess) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+attn_status attn_decode_schedule_bytes(const attn_desc* desc, int32_t window, size_t* bytes) {
+  if (bytes == nullptr) return ATTN_ERR_NULL;
+  const attn_status s = check_desc(desc);
+  if (s != ATTN_OK) return s;
+  *bytes = uses_split_decode(desc) ? decode_schedule_bytes_for(desc, window) : 0;
+  return ATTN_OK;
+}
+
+attn_status attn_build_decode_schedule(const attn_desc* desc, const int32_t* seq_lens,
+                                       int32_t window, int32_t* schedule,
+                                       size_t schedule_bytes, void* stream) {
+  size_t need = 0;
+  const attn_status s = attn_decode_schedule_bytes(desc, window, &need);
+  if (s != ATTN_OK) return s;
+  if (need == 0) return ATTN_OK;                 // no split-KV decode rows: nothing to build
+  if (schedule == nullptr || schedule_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (seq_lens == nullptr) return ATTN_ERR_NULL;
+  attn::DecodeScheduleParams sp{};
+  sp.seq_lens = seq_lens;
+  sp.schedule = schedule;
+  sp.num_decodes = desc->num_decodes;
+  sp.part_tokens = partition_tokens(desc);
+  sp.max_parts = (int32_t)decode_max_parts(desc, window);
+  sp.window = window > 0 ? window : 0;
+  sp.kv_skip_keys = 0;
+  return attn::launch_decode_schedule(sp, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_varlen_fwd_prescheduled(
+    const attn_desc* desc, const void* q, const void* kv_cache, const int32_t* block_table,
+    const int32_t* query_start_loc, const int32_t* seq_lens, float scale, int32_t causal,
+    int32_t window, void* out, float* lse, void* workspace, size_t workspace_bytes,
+    const int32_t* prefill_schedule, size_t prefill_schedule_bytes,
+    const int32_t* decode_schedule, size_t decode_schedule_bytes, void* stream) {
+  attn_status s = check_desc(desc);
+  if (s != ATTN_OK) return s;
+  const attn_desc& d = *desc;
+  if (window > 0 && !causal) return ATTN_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (prefill_schedule != nullptr) {
+    if (d.dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    size_t need_sched = 0;
+    s = attn_schedule_bytes(desc, &need_sched);
+    if (s != ATTN_OK) return s;
+    if (prefill_schedule_bytes < need_sched) return ATTN_ERR_WORKSPACE;
+  }
+  if (decode_schedule != nullptr && uses_split_decode(&d) &&
+      decode_schedule_bytes < decode_schedule_bytes_for(&d, window))
+    return ATTN_ERR_WORKSPACE;
+  if (d.num_seqs == 0 || d.num_tokens == 0) return ATTN_OK;
+  if (q == nullptr || kv_cache == nullptr || block_table == nullptr ||
+      query_start_loc == nullptr || seq_lens == nullptr || out == nullptr)
+    return ATTN_ERR_NULL;
+  const int64_t max_parts = decode_max_parts(&d, window);
+  const size_t need = workspace_for(&d, max_parts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  attn::PrefillParams pp = prefill_params(d, q, kv_cache, block_table, query_start_loc,
+                                          seq_lens, scale, causal, window, out, lse);
+  if (d.dtype == ATTN_F32) {
+    pp.seq_begin = 0;
+    pp.num_seqs = d.num_seqs;
+    return attn::launch_prefill_f32(pp, st) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  }
+  if (d.num_decodes > 0) {
+    attn::DecodeParams dp = decode_params(d, pp, max_parts, static_cast<float*>(workspace));
+    dp.items = decode_schedule;                   // null: the launch builds it in the workspace
+    if (attn::launch_decode_bf16(dp, st) != hipSuccess) return ATTN_ERR_HIP;
+  }
+  if (d.num_seqs > d.num_decodes) {
+    pp.seq_begin = d.num_decodes;
+    pp.num_seqs = d.num_seqs - d.num_decodes;
+    if (prefill_schedule != nullptr) {
+      pp.schedule = prefill_schedule;
+      pp.max_qtiles = (int32_t)schedule_max_qtiles(&d);
+    }
     if (attn::launch_prefill_bf16(pp, st) != hipSuccess) return ATTN_ERR_HIP;
   }
   return ATTN_OK;

@@ -2,20 +2,20 @@
 //
 // Method: the RBLN "Attention 모드" page (Overview, Flash Attention bullet) processes each
 // request's KV cache partition by partition and combines the per-partition results with online
-// softmax. Here one workgroup handles one (decode request, kv head, partition of
-// part_tokens keys) and all q heads that share that kv head (num_queries_per_kv of the vLLM
+// softmax. Here one unit of work is one (decode request, kv head, partition of part_tokens
+// keys) with all q heads that share that kv head (num_queries_per_kv of the vLLM
 // FlashAttention page's FlashAttentionImpl section), so every K/V byte is read from HBM once
 // per kv head. The partition result (normalised output and its lse) goes to the workspace,
 // and a second kernel merges the partitions of each (request, q head) through their
 // log-sum-exp. A request whose visible keys fit one partition is written directly.
 //
-// Inside a workgroup each of the 4 waves streams its own quarter of the partition in 32-key
-// chunks, with the next chunk's loads issued before the current chunk's math:
-//   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: K rows go straight from HBM into the A
-//     operand (16-byte loads), the q heads of the group sit in the 16 MFMA columns;
+// A unit runs on one wave (partitions of up to 1024 keys) or on a 4-wave workgroup whose
+// waves take a quarter of the partition each and combine through LDS (longer partitions).
+// A wave streams its keys in 32-key chunks, two chunks' loads in flight ahead of the math:
+//   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16, the q heads of the group in the 16 MFMA
+//     columns;
 //   * V rows are copied into a wave-private LDS tile and read back transposed with
-//     ds_read_b64_tr_b16 as the A operand of O^T += V^T . P^T;
-//   * the 4 waves' (max, sum, O) are combined through LDS at the end.
+//     ds_read_b64_tr_b16 as the A operand of O^T += V^T . P^T.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -26,6 +26,10 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kChunk = 32;       // keys per wave iteration
+// Partitions of at most this many keys run one per wave (decode_wave_kernel), longer ones one
+// per workgroup (decode_split_kernel). With block_size >= 16 a partition of 1024 keys spans
+// at most 64 blocks, one per lane.
+constexpr int kWavePartMax = 1024;
 
 // 8 E4M3 codes (two 32-bit words) -> 8 bf16 values, exactly (every E4M3 value is a bf16
 // value; v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts two codes, checked on gfx950 for all
@@ -39,108 +43,81 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// FP8 = true: the cache holds E4M3 codes (one byte per element) with per-tensor scales; the
-// host folds k_scale into p.scale and the kernel multiplies the output by p.v_scale.
+// Q^T (B operand of the QK^T product) for q heads h0 .. h0 + nh - 1 of token tok: lane
+// (G, li) holds q head h0 + li at the d values its K operand holds: d = 32c + 8G .. +7 (bf16),
+// or d = 64(c/2) + 16G + 8(c%2) .. +7 for E4M3 K, where lane G reads bytes 64w + 16G .. +15 of
+// the row with load w, so that each load instruction covers 64 contiguous bytes of 16 rows
+// (any fixed order of d is the same dot product). Lanes past nh hold zeros.
 template <int D, bool FP8>
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams p) {
-  constexpr int RS = D + 16;           // LDS row stride (bf16) of a V chunk
+__device__ __forceinline__ void load_q_frag(const DecodeParams& p, int tok, int h0, int nh,
+                                            bf16x8 (&qf)[D / 32]) {
+  const int lane = threadIdx.x % kWave;
+  const int G = lane / 16;
+  const int li = lane % 16;
+  const __bf16* __restrict__ q = static_cast<const __bf16*>(p.q);
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    const int d0 = FP8 ? 64 * (c / 2) + 16 * G + 8 * (c % 2) : 32 * c + 8 * G;
+    qf[c] = li < nh ? *reinterpret_cast<const bf16x8*>(
+                          q + ((int64_t)tok * p.num_heads + h0 + li) * D + d0)
+                    : bf16x8{};
+  }
+}
+
+// LDS one wave uses while streaming: a V chunk tile (read back transposed) and, for bf16, a K
+// chunk tile (bf16 elements each).
+template <int D>
+struct WaveTiles {
+  static constexpr int RS = D + 16;            // row stride of a V chunk
+  static constexpr int V_TILE = kChunk * RS;
+  // bf16 K also goes through a wave-private LDS tile: its rows are loaded like V's (whole
+  // 256-byte rows, 4 per instruction), which streams about 9 % faster on gfx950 than loading
+  // the MFMA operand layout straight from HBM (16 rows x 64 bytes per instruction)
+  static constexpr int KRS = D + 8;            // row stride of a K chunk
+  static constexpr int K_TILE = kChunk * KRS;
+};
+
+// One wave's online-softmax pass over the keys [w_begin, w_end) of a decode request, for the
+// q heads whose Q^T fragment is qf (kv head kvh), in 32-key chunks aligned to c_base (the
+// chunk of w_begin is the first one). last_key is the request's last key in this partition:
+// loads past it read that key's group again (clamped), so every load reads a valid row of the
+// request; keys outside [w_begin, w_end) get score -inf. block_of(b) gives the cache block of
+// the request's b-th block of this pass. Returns, per lane (G, li), the running max m_run and
+// this lane's share of the running sum l_run (scores of column li; m_run is the same in
+// every lane of a column), and O^T: o[dc][e] = sum_j p_j V[j][16 dc + 4 G + e] for q head
+// li, unnormalised.
+//   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (K rows in the A operand, q heads in the 16
+//     columns);
+//   * V rows are copied into the wave's LDS tile and read back transposed with
+//     ds_read_b64_tr_b16 as the A operand of O^T += V^T . P^T.
+template <int D, bool FP8, class BlockOf>
+__device__ __forceinline__ void stream_keys(const DecodeParams& p, int kvh,
+                                            const bf16x8 (&qf)[D / 32], int c_base, int w_begin,
+                                            int w_end, int last_key, BlockOf block_of,
+                                            __bf16* sVw, __bf16* sKw, float& m_run,
+                                            float& l_run, floatx4 (&o)[D / 16]) {
+  using T = WaveTiles<D>;
+  constexpr int RS = T::RS;
+  constexpr int KRS = T::KRS;
   constexpr int KC = D / 32;
   constexpr int DC = D / 16;
   constexpr int EPL = FP8 ? 16 : 8;    // V elements per lane and copy instruction (16 bytes)
   constexpr int TPR = D / EPL;         // lanes per V row in the copy
   constexpr int RPI = kWave / TPR;     // V rows per copy instruction
   constexpr int NV = kChunk / RPI;     // copy instructions per chunk
-  constexpr int V_TILE = kChunk * RS;  // bf16 per wave tile
-  // bf16 K also goes through a wave-private LDS tile: its rows are loaded like V's (whole
-  // 256-byte rows, 4 per instruction), which streams about 9 % faster on gfx950 than loading
-  // the MFMA operand layout straight from HBM (16 rows x 64 bytes per instruction)
-  constexpr int KRS = D + 8;           // LDS row stride (bf16) of a K chunk
-  constexpr int K_TILE = kChunk * KRS;
-  constexpr int OS = D + 4;            // fp32 row stride of the combine buffer
-
-  // V tiles during the stream; reused as the combine buffer afterwards
-  constexpr int kLdsBytes = (kWaves * V_TILE * 2 > kWaves * 16 * OS * 4)
-                                ? kWaves * V_TILE * 2 : kWaves * 16 * OS * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-  __shared__ float sM[kWaves][16];
-  __shared__ float sL[kWaves][16];
-  __shared__ int32_t sBlk[kMaxPartitionTokens / 16];   // block ids of this partition
-  __shared__ __attribute__((aligned(16))) __bf16 sK[FP8 ? 8 : kWaves * K_TILE];
-
-  // grid x = item slot * heads_wg + (kv head, head group): the workgroups of one item read
-  // the same tokens' rows (adjacent in every cache block) side by side, and the items come
-  // from the decode schedule, longest partition first
-  const int group = p.num_heads / p.num_kv_heads;
-  const int head_groups = (group + 15) / 16;
-  const int heads_wg = p.num_kv_heads * head_groups;
-  const int slot = blockIdx.x / heads_wg;
-  const int count = p.schedule[0];
-  const int item = p.schedule[1 + min(slot, p.num_decodes * p.max_parts - 1)];
-  if (slot >= count) return;
-  const int r = item / p.max_parts;
-  const int pi = item % p.max_parts;
-  const int kvh = (blockIdx.x % heads_wg) / head_groups;
-  const int hg = blockIdx.x % head_groups;
-  const int nh = min(16, group - hg * 16);             // q heads in this workgroup
-  const int h0 = kvh * group + hg * 16;                // first q head
-
-  // keys of this pass: [0, sl) after skipping kv_skip_blocks leading blocks
-  const int sl = p.seq_lens[r] - p.kv_skip_blocks * p.block_size;
-  int first, nparts;
-  decode_partitions(sl, p.window, p.part_tokens, &first, &nparts);
-  nparts = min(nparts, p.max_parts);   // only reachable with seq_len > max_seq_len
-  const int part = first + pi;
-  const int p_start = part * p.part_tokens;
-  const int lo = p.window > 0 ? max(0, sl - p.window) : 0;
-  const int k_begin = max(lo, p_start);
-  const int k_end = min(sl, p_start + p.part_tokens);
-  const int tok = p.qsl[r];
-
-  const int tid = threadIdx.x;
-  const int w = tid / kWave;
-  const int lane = tid % kWave;
+  const int lane = threadIdx.x % kWave;
   const int G = lane / 16;
   const int li = lane % 16;
+  const int v_row = lane / TPR;
+  const int v_chunk = lane % TPR;
 
-  // block ids covering [p_start, k_end) -> LDS, so the K/V loads need no dependent lookup
-  const int b_first = p_start / p.block_size;
-  const int n_blk = (k_end - 1) / p.block_size - b_first + 1;
-  const int32_t* __restrict__ bt = p.block_table + (int64_t)r * p.max_blocks + p.kv_skip_blocks;
-  for (int i = tid; i < n_blk; i += 256) sBlk[i] = bt[b_first + i];
-
-  const __bf16* __restrict__ q = static_cast<const __bf16*>(p.q);
-  typedef typename std::conditional<FP8, uint8_t, __bf16>::type kv_t;
-  const kv_t* __restrict__ kcache = static_cast<const kv_t*>(p.kv);
-  const kv_t* __restrict__ vcache = kcache + p.v_offset;
-
-  // Q^T (B operand): lane (G, li) holds q head h0 + li at the d values its K operand holds:
-  // d = 32c + 8G .. +7 (bf16), or d = 64(c/2) + 16G + 8(c%2) .. +7 for E4M3 K, where lane G
-  // reads bytes 64w + 16G .. +15 of the row with load w, so that each load instruction covers
-  // 64 contiguous bytes of 16 rows (any fixed order of d is the same dot product)
-  bf16x8 qf[KC];
-#pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    const int d0 = FP8 ? 64 * (c / 2) + 16 * G + 8 * (c % 2) : 32 * c + 8 * G;
-    qf[c] = li < nh ? *reinterpret_cast<const bf16x8*>(
-                          q + ((int64_t)tok * p.num_heads + h0 + li) * D + d0)
-                    : bf16x8{};
-  }
-
-  // this wave's key range: quarter w of the partition, clipped to the visible range
-  const int quarter = p.part_tokens / kWaves;
-  const int w_begin = max(k_begin, p_start + w * quarter);
-  const int w_end = min(k_end, p_start + (w + 1) * quarter);
-  // chunks are aligned to the quarter start (a multiple of 32)
-  const int c_base = p_start + w * quarter;
   const int c_first = w_end > w_begin ? (w_begin - c_base) / kChunk : 0;
   const int n_chunks =
       w_end > w_begin ? (w_end - (c_base + c_first * kChunk) + kChunk - 1) / kChunk : 0;
 
-  __bf16* sVw = reinterpret_cast<__bf16*>(lds) + w * V_TILE;
-  __bf16* sKw = sK + (FP8 ? 0 : w * K_TILE);
-  const int v_row = lane / TPR;
-  const int v_chunk = lane % TPR;
-  __syncthreads();   // sBlk ready
+  typedef typename std::conditional<FP8, uint8_t, __bf16>::type kv_t;
+  const kv_t* __restrict__ kcache = static_cast<const kv_t*>(p.kv);
+  const kv_t* __restrict__ vcache = kcache + p.v_offset;
 
   // raw K / V of one chunk: bf16 K as whole rows like V (instruction j = k[j / KW][j % KW]),
   // E4M3 K as D/64 16-byte words per lane (word w at byte 64w + 16G); V as 16 bytes per lane and
@@ -153,24 +130,22 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
     u32x4 v[NV];
   };
   // Element offset of the first row of the 16-key group starting at key g0 (clamped to the
-  // last visible group, so every load below reads a valid row of this request). A 16-key
-  // group lies in one block (block_size is a multiple of 16); the block index comes from
-  // the partition's ids in LDS and the host's 32.32 reciprocal of block_size / 16.
-  const int last_key = k_end - 1;
+  // last visible group). A 16-key group lies in one block (block_size is a multiple of 16);
+  // the block index comes from the host's 32.32 reciprocal of block_size / 16.
   const int last_group = last_key & ~15;
   const uint32_t block_elems = (uint32_t)(p.block_size * p.num_kv_heads * D);   // < 2^31
   const int kv_row = p.num_kv_heads * D;
-  auto group_off = [&](int g0, int* first_key) {
+  auto group_off = [&](int g0, int* first_key) __attribute__((always_inline)) {
     g0 = min(g0, last_group);
     *first_key = g0;
     const uint32_t bidx = (uint32_t)(((uint64_t)(uint32_t)(g0 >> 4) * p.group_recip) >> 32);
-    const int32_t blk = sBlk[bidx - b_first];
+    const int32_t blk = block_of(bidx);
     return (uint64_t)(uint32_t)blk * block_elems +
            (uint32_t)((g0 - (int)bidx * p.block_size) * kv_row + kvh * D);
   };
   // keys past the wave's range load a valid row (clamped); their scores are masked, so they
   // add 0 * (finite V) and need no zeroing
-  auto load_chunk = [&](Chunk& ch, int kb) {
+  auto load_chunk = [&](Chunk& ch, int kb) __attribute__((always_inline)) {
     if constexpr (FP8) {
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
@@ -201,13 +176,13 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   };
 
   const float c_log2 = p.scale * kLog2e;
-  float m_run = -INFINITY, l_run = 0.f;
-  floatx4 o[DC];
+  m_run = -INFINITY;
+  l_run = 0.f;
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) o[dc] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // consume chunk ci held in ch; after its QK^T MFMAs, refill ch with chunk ci + 2
-  auto consume = [&](Chunk& ch, int ci) {
+  auto consume = [&](Chunk& ch, int ci) __attribute__((always_inline)) {
     const int kb = c_base + (c_first + ci) * kChunk;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -300,8 +275,106 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
     for (int b = 0; b < kInFlight; ++b)
       if (ci + b < n_chunks) consume(buf[b], ci + b);
   }
+}
+
+// The decode work item in schedule slot `slot` for (kv head, head group) `hw`, and the keys it
+// reads. valid is false for slots past the item count.
+struct DecodeItem {
+  bool valid;
+  int r, pi, hw, kvh, nh, h0, tok;
+  int nparts;                    // partitions of the request holding visible keys
+  int p_start, k_begin, k_end;   // partition start, visible keys [k_begin, k_end)
+};
+__device__ __forceinline__ DecodeItem decode_item(const DecodeParams& p, int slot, int hw) {
+  DecodeItem it{};
+  const int group = p.num_heads / p.num_kv_heads;
+  const int head_groups = (group + 15) / 16;
+  const int count = p.items[0];
+  const int item = p.items[1 + min(slot, p.num_decodes * p.max_parts - 1)];
+  it.valid = slot < count;
+  if (!it.valid) return it;
+  it.r = item / p.max_parts;
+  it.pi = item % p.max_parts;
+  it.hw = hw;
+  it.kvh = hw / head_groups;
+  const int hg = hw % head_groups;
+  it.nh = min(16, group - hg * 16);                   // q heads of this unit
+  it.h0 = it.kvh * group + hg * 16;                   // first q head
+  // keys of this pass: [0, sl) after skipping kv_skip_blocks leading blocks
+  const int sl = p.seq_lens[it.r] - p.kv_skip_blocks * p.block_size;
+  int first;
+  decode_partitions(sl, p.window, p.part_tokens, &first, &it.nparts);
+  it.nparts = min(it.nparts, p.max_parts);   // only reachable with seq_len > max_seq_len
+  it.p_start = (first + it.pi) * p.part_tokens;
+  const int lo = p.window > 0 ? max(0, sl - p.window) : 0;
+  it.k_begin = max(lo, it.p_start);
+  it.k_end = min(sl, it.p_start + p.part_tokens);
+  it.tok = p.qsl[it.r];
+  return it;
+}
+
+// FP8 = true: the cache holds E4M3 codes (one byte per element) with per-tensor scales; the
+// host folds k_scale into p.scale and the kernel multiplies the output by p.v_scale.
+//
+// Workgroup mode (partitions of more than kWavePartMax keys): one workgroup of 4 waves per
+// (item, kv head, head group); each wave streams its own quarter of the partition and the 4
+// waves' (max, sum, O) are combined through LDS at the end.
+template <int D, bool FP8>
+__global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams p) {
+  using T = WaveTiles<D>;
+  constexpr int OS = D + 4;            // fp32 row stride of the combine buffer
+  // V tiles during the stream; reused as the combine buffer afterwards
+  constexpr int kLdsBytes = (kWaves * T::V_TILE * 2 > kWaves * 16 * OS * 4)
+                                ? kWaves * T::V_TILE * 2 : kWaves * 16 * OS * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  __shared__ float sM[kWaves][16];
+  __shared__ float sL[kWaves][16];
+  __shared__ int32_t sBlk[kMaxPartitionTokens / 16];   // block ids of this partition
+  __shared__ __attribute__((aligned(16))) __bf16 sK[FP8 ? 8 : kWaves * T::K_TILE];
+
+  // grid x = item slot * heads_wg + (kv head, head group): the workgroups of one item read
+  // the same tokens' rows (adjacent in every cache block) side by side, and the items come
+  // from the decode schedule, longest partition first
+  const int heads_wg = p.num_kv_heads * ((p.num_heads / p.num_kv_heads + 15) / 16);
+  const DecodeItem it = decode_item(p, blockIdx.x / heads_wg, blockIdx.x % heads_wg);
+  if (!it.valid) return;
+
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int lane = tid % kWave;
+  const int G = lane / 16;
+  const int li = lane % 16;
+
+  // block ids covering [p_start, k_end) -> LDS, so the K/V loads need no dependent lookup
+  const int b_first = it.p_start / p.block_size;
+  const int n_blk = (it.k_end - 1) / p.block_size - b_first + 1;
+  const int32_t* __restrict__ bt =
+      p.block_table + (int64_t)it.r * p.max_blocks + p.kv_skip_blocks;
+  for (int i = tid; i < n_blk; i += 256) sBlk[i] = bt[b_first + i];
+
+  bf16x8 qf[D / 32];
+  load_q_frag<D, FP8>(p, it.tok, it.h0, it.nh, qf);
+
+  // this wave's key range: quarter w of the partition, clipped to the visible range; chunks
+  // are aligned to the quarter start (a multiple of 32)
+  const int quarter = p.part_tokens / kWaves;
+  const int c_base = it.p_start + w * quarter;
+  const int w_begin = max(it.k_begin, c_base);
+  const int w_end = min(it.k_end, c_base + quarter);
+  __bf16* sVw = reinterpret_cast<__bf16*>(lds) + w * T::V_TILE;
+  __bf16* sKw = sK + (FP8 ? 0 : w * T::K_TILE);
+  __syncthreads();   // sBlk ready
+
+  float m_run, l_run;
+  floatx4 o[D / 16];
+  stream_keys<D, FP8>(p, it.kvh, qf, c_base, w_begin, w_end, it.k_end - 1,
+                      [&](uint32_t bidx) __attribute__((always_inline)) {
+                        return sBlk[bidx - b_first];
+                      },
+                      sVw, sKw, m_run, l_run, o);
 
   // ---- combine the 4 waves: (m, l, O^T) -> partition result
+  const float c_log2 = p.scale * kLog2e;
   const float l_w = column_sum(l_run);
   __syncthreads();   // every wave is done with its V tile; the LDS becomes the combine buffer
   float* sO = reinterpret_cast<float*>(lds);
@@ -310,14 +383,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
     sL[w][li] = l_w;
   }
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc)
+  for (int dc = 0; dc < D / 16; ++dc)
     *reinterpret_cast<floatx4*>(&sO[(w * 16 + li) * OS + 16 * dc + 4 * G]) = o[dc];
   __syncthreads();
 
   constexpr int DPT = D / 16;          // d values per thread: 256 threads = 16 heads x 16
   const int hh = tid / 16;             // head within the workgroup
   const int d0 = (tid % 16) * DPT;
-  if (hh >= nh) return;
+  if (hh >= it.nh) return;
   float M = -INFINITY;
 #pragma unroll
   for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sM[ww][hh]);
@@ -339,14 +412,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
     acc[x] = FP8 ? a * inv * p.v_scale : a * inv;
   }
   const float lse_part = L > 0.f ? p.scale * M + __logf(L) : -INFINITY;
-  const int hq = h0 + hh;
-  if (nparts == 1 && p.pre_o == nullptr) {
-    __bf16* dst = static_cast<__bf16*>(p.out) + ((int64_t)tok * p.num_heads + hq) * D + d0;
+  const int hq = it.h0 + hh;
+  if (it.nparts == 1 && p.pre_o == nullptr) {
+    __bf16* dst = static_cast<__bf16*>(p.out) + ((int64_t)it.tok * p.num_heads + hq) * D + d0;
 #pragma unroll
     for (int x = 0; x < DPT; ++x) dst[x] = to_bf16(acc[x]);
-    if (p.lse != nullptr && d0 == 0) p.lse[(int64_t)tok * p.num_heads + hq] = lse_part;
+    if (p.lse != nullptr && d0 == 0) p.lse[(int64_t)it.tok * p.num_heads + hq] = lse_part;
   } else {
-    const int64_t slot = ((int64_t)r * p.num_heads + hq) * p.max_parts + pi;
+    const int64_t slot = ((int64_t)it.r * p.num_heads + hq) * p.max_parts + it.pi;
     float* dst = p.ws_o + slot * D + d0;
 #pragma unroll
     for (int x = 0; x < DPT; x += 4)
@@ -355,8 +428,78 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
   }
 }
 
-// One wave per (q head, decode request): out = sum_p exp(lse_p - L) o_p, lse = L, over the
-// request's partitions plus, in a cascade suffix pass, the prefix's partial result.
+// Wave mode (partitions of at most kWavePartMax keys): each wave of a 4-wave workgroup is one
+// (item, kv head, head group) unit and streams the whole partition alone, so no cross-wave
+// combine and no barrier; the partition's block ids (at most 64) sit one per lane and reach
+// the address computation through v_readlane. Units are numbered like the workgroup mode's
+// grid (item slot * heads_wg + (kv head, head group)), 4 consecutive units per workgroup.
+template <int D, bool FP8>
+__global__ __launch_bounds__(256, 2) void decode_wave_kernel(const DecodeParams p) {
+  using T = WaveTiles<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 sV[kWaves * T::V_TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[FP8 ? 8 : kWaves * T::K_TILE];
+
+  const int w = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int G = lane / 16;
+  const int li = lane % 16;
+  const int heads_wg = p.num_kv_heads * ((p.num_heads / p.num_kv_heads + 15) / 16);
+  const int unit = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + w);
+  const DecodeItem it = decode_item(p, unit / heads_wg, unit % heads_wg);
+  if (!it.valid) return;
+
+  // lane i holds the cache block of the partition's i-th block (n_blk <= 64: the partition
+  // has at most kWavePartMax keys and block_size is a multiple of 16)
+  const int b_first = it.p_start / p.block_size;
+  const int n_blk = (it.k_end - 1) / p.block_size - b_first + 1;
+  const int32_t* __restrict__ bt =
+      p.block_table + (int64_t)it.r * p.max_blocks + p.kv_skip_blocks;
+  const int32_t blk_lane = lane < n_blk ? bt[b_first + lane] : 0;
+
+  bf16x8 qf[D / 32];
+  load_q_frag<D, FP8>(p, it.tok, it.h0, it.nh, qf);
+
+  float m_run, l_run;
+  floatx4 o[D / 16];
+  stream_keys<D, FP8>(p, it.kvh, qf, it.p_start, it.k_begin, it.k_end, it.k_end - 1,
+                      [&](uint32_t bidx) __attribute__((always_inline)) {
+                        return __builtin_amdgcn_readlane(blk_lane, (int)(bidx - b_first));
+                      },
+                      sV + w * T::V_TILE, sK + (FP8 ? 0 : w * T::K_TILE), m_run, l_run, o);
+
+  // lane (G, li) holds O^T rows d = 16 dc + 4 G .. +3 of q head h0 + li
+  const float l = column_sum(l_run);
+  if (li >= it.nh) return;
+  const float inv = l > 0.f ? (FP8 ? p.v_scale : 1.f) / l : 0.f;
+  const float lse_part = l > 0.f ? p.scale * m_run + __logf(l) : -INFINITY;
+  const int hq = it.h0 + li;
+  if (it.nparts == 1 && p.pre_o == nullptr) {
+    __bf16* dst = static_cast<__bf16*>(p.out) + ((int64_t)it.tok * p.num_heads + hq) * D;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) {
+      const floatx4 v = o[dc] * inv;
+      bf16x4 b4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b4[e] = to_bf16(v[e]);
+      *reinterpret_cast<bf16x4*>(dst + 16 * dc + 4 * G) = b4;
+    }
+    if (p.lse != nullptr && G == 0) p.lse[(int64_t)it.tok * p.num_heads + hq] = lse_part;
+  } else {
+    const int64_t slot = ((int64_t)it.r * p.num_heads + hq) * p.max_parts + it.pi;
+    float* dst = p.ws_o + slot * D;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc)
+      *reinterpret_cast<floatx4*>(dst + 16 * dc + 4 * G) = o[dc] * inv;
+    if (G == 0) p.ws_lse[slot] = lse_part;
+  }
+}
+
+// One wave per (q head, decode request): out = sum_p exp(lse_p - L) o_p and lse = L =
+// log sum_p exp(lse_p) over the request's partitions plus, in a cascade suffix pass, the
+// prefix's partial result. The partitions are read kMergeBatch at a time with all their loads
+// in flight together, and folded into a running (max, sum, weighted output), so a merge takes
+// one memory round trip per kMergeBatch partitions.
+constexpr int kMergeBatch = 16;
 template <int D>
 __global__ __launch_bounds__(64) void lse_merge_kernel(const DecodeParams p) {
   const int hq = blockIdx.x;
@@ -371,62 +514,86 @@ __global__ __launch_bounds__(64) void lse_merge_kernel(const DecodeParams p) {
   const int tok = p.qsl[r];
   const int64_t base = ((int64_t)r * p.num_heads + hq) * p.max_parts;
   const int64_t row = (int64_t)tok * p.num_heads + hq;
-  const float lse_pre = pre ? p.pre_lse[row] : -INFINITY;
-  float M = lse_pre;
-  for (int pi = lane; pi < nparts; pi += kWave) M = fmaxf(M, p.ws_lse[base + pi]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  const float M_use = (M == -INFINITY) ? 0.f : M;
-  float S = 0.f;
-  for (int pi = lane; pi < nparts; pi += kWave) S += fast_exp2((p.ws_lse[base + pi] - M_use) * kLog2e);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
-  S += fast_exp2((lse_pre - M_use) * kLog2e);          // 0 without a prefix
-  const float L = S > 0.f ? M_use + __logf(S) : -INFINITY;
   constexpr int DPL = D / kWave;
+  float m = -INFINITY, s = 0.f;
   float acc[DPL];
 #pragma unroll
   for (int x = 0; x < DPL; ++x) acc[x] = 0.f;
-  for (int pi = 0; pi < nparts; ++pi) {
-    const float wgt = S > 0.f ? fast_exp2((p.ws_lse[base + pi] - L) * kLog2e) : 0.f;
-    const float* src = p.ws_o + (base + pi) * D;
+  if (pre) {
+    const float lp = p.pre_lse[row];
+    if (lp != -INFINITY) {
+      m = lp;
+      s = 1.f;
 #pragma unroll
-    for (int x = 0; x < DPL; ++x) acc[x] += wgt * src[lane + kWave * x];
+      for (int x = 0; x < DPL; ++x) acc[x] = p.pre_o[row * D + lane + kWave * x];
+    }
   }
-  if (pre && S > 0.f) {
-    const float wgt = fast_exp2((lse_pre - L) * kLog2e);
-    const float* src = p.pre_o + row * D;
+  for (int p0 = 0; p0 < nparts; p0 += kMergeBatch) {
+    float l[kMergeBatch], v[kMergeBatch][DPL];
 #pragma unroll
-    for (int x = 0; x < DPL; ++x) acc[x] += wgt * src[lane + kWave * x];
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int64_t slot = base + min(p0 + i, nparts - 1);   // past the end: masked below
+      l[i] = p.ws_lse[slot];
+#pragma unroll
+      for (int x = 0; x < DPL; ++x) v[i][x] = p.ws_o[slot * D + lane + kWave * x];
+    }
+    float mb = m;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i)
+      if (p0 + i < nparts) mb = fmaxf(mb, l[i]);
+    const float mu = (mb == -INFINITY) ? 0.f : mb;
+    const float a = fast_exp2((m - mu) * kLog2e);          // 0 while nothing is merged
+    s *= a;
+#pragma unroll
+    for (int x = 0; x < DPL; ++x) acc[x] *= a;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (p0 + i >= nparts) break;
+      const float w = fast_exp2((l[i] - mu) * kLog2e);
+      s += w;
+#pragma unroll
+      for (int x = 0; x < DPL; ++x) acc[x] += w * v[i][x];
+    }
+    m = mb;
   }
+  const float inv = s > 0.f ? 1.f / s : 0.f;
   __bf16* dst = static_cast<__bf16*>(p.out) + row * D;
 #pragma unroll
-  for (int x = 0; x < DPL; ++x) dst[lane + kWave * x] = to_bf16(acc[x]);
-  if (p.lse != nullptr && lane == 0) p.lse[row] = L;
+  for (int x = 0; x < DPL; ++x) dst[lane + kWave * x] = to_bf16(acc[x] * inv);
+  if (p.lse != nullptr && lane == 0) p.lse[row] = s > 0.f ? m + __logf(s) : -INFINITY;
 }
 
-// The schedule kernel, then one workgroup per (schedule slot, kv head, head group) (slots past
-// the item count exit at once), then the merge. The schedule lives in the caller's workspace.
+// The schedule kernel (unless the caller built the schedule ahead), then the split kernel
+// (one wave or workgroup per (schedule slot, kv head, head group), slots past the item count
+// exiting at once), then the merge.
 template <int D, bool FP8>
 hipError_t launch(const DecodeParams& p, hipStream_t stream) {
-  const int group = p.num_heads / p.num_kv_heads;
-  const int head_groups = (group + 15) / 16;
-  DecodeScheduleParams sp{};
-  sp.seq_lens = p.seq_lens;
-  sp.schedule = p.schedule;         // written here, read by the split kernel
-  sp.num_decodes = p.num_decodes;
-  sp.part_tokens = p.part_tokens;
-  sp.max_parts = p.max_parts;
-  sp.window = p.window;
-  sp.kv_skip_keys = p.kv_skip_blocks * p.block_size;
-  hipError_t e = launch_decode_schedule(sp, stream);
-  if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((int64_t)p.num_decodes * p.max_parts * p.num_kv_heads * head_groups));
-  hipLaunchKernelGGL((decode_split_kernel<D, FP8>), grid, dim3(256), 0, stream, p);
-  e = hipGetLastError();
+  const int head_groups = (p.num_heads / p.num_kv_heads + 15) / 16;
+  DecodeParams pk = p;
+  if (pk.items == nullptr) {
+    DecodeScheduleParams sp{};
+    sp.seq_lens = p.seq_lens;
+    sp.schedule = p.schedule;
+    sp.num_decodes = p.num_decodes;
+    sp.part_tokens = p.part_tokens;
+    sp.max_parts = p.max_parts;
+    sp.window = p.window;
+    sp.kv_skip_keys = p.kv_skip_blocks * p.block_size;
+    const hipError_t e = launch_decode_schedule(sp, stream);
+    if (e != hipSuccess) return e;
+    pk.items = p.schedule;
+  }
+  const int64_t units = (int64_t)p.num_decodes * p.max_parts * p.num_kv_heads * head_groups;
+  if (p.part_tokens <= kWavePartMax)
+    hipLaunchKernelGGL((decode_wave_kernel<D, FP8>), dim3((unsigned)((units + kWaves - 1) / kWaves)),
+                       dim3(256), 0, stream, pk);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, FP8>), dim3((unsigned)units), dim3(256), 0,
+                       stream, pk);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess || (p.max_parts <= 1 && p.pre_o == nullptr)) return e;
   hipLaunchKernelGGL(lse_merge_kernel<D>, dim3(p.num_heads, p.num_decodes), dim3(kWave), 0,
-                     stream, p);
+                     stream, pk);
   return hipGetLastError();
 }
 

@@ -65,8 +65,11 @@ struct DecodeParams {
   uint64_t group_recip;         // ceil(2^32 / (block_size / 16)), as in PrefillParams
   float v_scale;                // E4M3 cache only: V dequantisation scale (k_scale is folded
                                 // into scale by the host)
-  int32_t* schedule;            // work items, longest first (see DecodeScheduleParams): grid
-                                // x = item slot * (num_kv_heads * head groups) + kv head group
+  int32_t* schedule;            // where the launch builds this call's work items (see
+                                // DecodeScheduleParams), unless items is set
+  const int32_t* items;         // the items the split kernel reads, longest first: schedule,
+                                // or a schedule the caller built ahead (then nothing is built);
+                                // unit = item slot * (num_kv_heads * head groups) + kv head group
   // Cascade suffix pass (zero / null for a plain call):
   int32_t kv_skip_blocks;       // as in PrefillParams
   const float* pre_o;           // non-null: a partial result over the prefix, fp32

@@ -12,9 +12,9 @@
 // Schedule buffer (int32): [0] = number of items n, [1 + i] = item i (i < n) as
 // request_offset * max_qtiles + q_tile, request_offset counting from the first prefill request.
 //
-// The split-KV decode kernel gets the same treatment on every call: its items are (decode
-// request, partition) pairs, sorted by their number of keys, so that the partial last
-// partitions of the requests run at the end of the grid instead of being spread over it.
+// The split-KV decode kernel gets the same treatment: its items are (decode request,
+// partition) pairs, sorted by their number of keys, so that the partial last partitions of the
+// requests run at the end of the grid instead of being spread over it.
 #include "device_common.hpp"
 #include "kernels.hpp"
 

@@ -96,6 +96,7 @@ typedef struct attn_desc {
  * where P is the number of partitions of max_seq_len (capped for a window in
  * attn_varlen_fwd), followed by the decode work schedule the call builds there:
  *   (1 + num_decodes * P) * 4 bytes, rounded up to 256.
+ * A workspace serves one call at a time (calls that share one must not overlap).
  * Returns 0 bytes when num_decodes == 0 or dtype is ATTN_F32.
  * Errors: ATTN_ERR_NULL (desc or bytes NULL), and the same shape checks as attn_varlen_fwd
  * that do not depend on the window.
@@ -349,6 +350,44 @@ attn_status attn_varlen_fwd_scheduled(const attn_desc* desc, const void* q, cons
                                       float* lse, void* workspace, size_t workspace_bytes,
                                       const int32_t* schedule, size_t schedule_bytes,
                                       void* stream);
+
+/*
+ * Decode work schedule built ahead of the attention call (the same [FA] FA3 reasoning as the
+ * prefill schedule above, applied to the split-KV decode rows whose partitions [RBLN] Overview
+ * combines by online softmax). attn_varlen_fwd builds this schedule in its workspace on every
+ * call with one small kernel: the (decode request, partition) items that hold visible keys,
+ * sorted by the number of keys each reads, longest first. It depends only on seq_lens, the
+ * window and the partition length, so a batch builds it once and every layer reuses it.
+ *
+ * attn_decode_schedule_bytes: bytes of the decode schedule buffer for `window`: the schedule
+ *   region of attn_workspace_bytes with P capped for the window; 0 when the call has no
+ *   split-KV decode rows (num_decodes == 0 or dtype ATTN_F32). Errors: ATTN_ERR_NULL and the
+ *   descriptor errors of attn_workspace_bytes.
+ * attn_build_decode_schedule: queue the kernel that writes the decode schedule (int32; element
+ *   0 is the item count, then the items) for the device array seq_lens. Does nothing when attn_decode_schedule_bytes gives 0. Errors: those of
+ *   attn_decode_schedule_bytes; ATTN_ERR_WORKSPACE when schedule is NULL or schedule_bytes
+ *   too small; ATTN_ERR_NULL for a NULL seq_lens.
+ * attn_varlen_fwd_prescheduled: attn_varlen_fwd that reads either schedule from the caller
+ *   instead of building it: prefill_schedule (bf16 only) from attn_build_schedule,
+ *   decode_schedule from attn_build_decode_schedule, each built for the same descriptor,
+ *   metadata, causal and window (not checked: it would need a device-to-host
+ *   synchronisation). Either may be NULL: that part is then scheduled as in attn_varlen_fwd.
+ *   A schedule is only read, so calls on any streams may share it. The workspace is still
+ *   attn_workspace_bytes(desc) (the decode partials live there). The results are identical
+ *   to attn_varlen_fwd's. Errors: those of attn_varlen_fwd, plus ATTN_ERR_WORKSPACE for a
+ *   schedule buffer below its size and ATTN_ERR_UNSUPPORTED for a prefill schedule with a
+ *   dtype other than ATTN_BF16.
+ */
+attn_status attn_decode_schedule_bytes(const attn_desc* desc, int32_t window, size_t* bytes);
+attn_status attn_build_decode_schedule(const attn_desc* desc, const int32_t* seq_lens,
+                                       int32_t window, int32_t* schedule,
+                                       size_t schedule_bytes, void* stream);
+attn_status attn_varlen_fwd_prescheduled(
+    const attn_desc* desc, const void* q, const void* kv_cache, const int32_t* block_table,
+    const int32_t* query_start_loc, const int32_t* seq_lens, float scale, int32_t causal,
+    int32_t window, void* out, float* lse, void* workspace, size_t workspace_bytes,
+    const int32_t* prefill_schedule, size_t prefill_schedule_bytes,
+    const int32_t* decode_schedule, size_t decode_schedule_bytes, void* stream);
 
 /* attn_status_str: static, NUL-terminated name of a status code ("ATTN_OK", ...). */
 const char* attn_status_str(int32_t status);

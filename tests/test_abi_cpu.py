@@ -333,6 +333,48 @@ def test_schedule_sizes_and_errors():
         A.ATTN_ERR_WORKSPACE
 
 
+def test_decode_schedule_sizes_and_errors():
+    """One count plus one slot per (decode, partition), the partitions capped for a window;
+    nothing to build without split-KV decode rows."""
+    d = _desc()                                        # 1 decode of <= 40 keys: 1 partition
+    assert A.attn_decode_schedule_bytes(d) == 256
+    assert A.attn_decode_schedule_bytes(_desc(dtype=A.ATTN_F32)) == 0
+    assert A.attn_decode_schedule_bytes(_desc(num_decodes=0)) == 0
+    long = _desc(num_seqs=64, num_tokens=64, num_decodes=64, max_query_len=1,
+                 max_seq_len=40000, num_blocks=4000, max_blocks_per_seq=2500,
+                 partition_tokens=256)
+    assert A.attn_decode_schedule_bytes(long) == -(-(4 * (1 + 64 * 157)) // 256) * 256
+    # a 1000-key window reaches at most ceil(1000 / 256) + 1 = 5 partitions
+    assert A.attn_decode_schedule_bytes(long, 1000) == -(-(4 * (1 + 64 * 5)) // 256) * 256
+    with pytest.raises(A.AttnError):
+        A.attn_decode_schedule_bytes(_desc(block_size=24))
+    lib = A.lib()
+    assert lib.attn_build_decode_schedule(ctypes.byref(d), FAKE, 0, None, 0, None) == \
+        A.ATTN_ERR_WORKSPACE
+    assert lib.attn_build_decode_schedule(ctypes.byref(d), FAKE, 0, FAKE, 255, None) == \
+        A.ATTN_ERR_WORKSPACE
+    assert lib.attn_build_decode_schedule(ctypes.byref(d), None, 0, FAKE, 256, None) == \
+        A.ATTN_ERR_NULL
+    # no split-KV decode rows: nothing to build, nothing touched
+    assert lib.attn_build_decode_schedule(ctypes.byref(_desc(num_decodes=0)), None, 0, None, 0,
+                                          None) == A.ATTN_OK
+
+    def pre(desc, ps, ps_bytes, ds, ds_bytes, causal=1, window=0):
+        return lib.attn_varlen_fwd_prescheduled(
+            ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, causal, window, FAKE, None,
+            FAKE, 1 << 20, ps, ps_bytes, ds, ds_bytes, None)
+    assert pre(d, None, 0, FAKE, 255) == A.ATTN_ERR_WORKSPACE      # decode schedule too small
+    assert pre(d, FAKE, 255, None, 0) == A.ATTN_ERR_WORKSPACE      # prefill schedule too small
+    assert pre(_desc(dtype=A.ATTN_F32), FAKE, 256, None, 0) == A.ATTN_ERR_UNSUPPORTED
+    assert pre(d, None, 0, None, 0, causal=0, window=8) == A.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_varlen_fwd_prescheduled(
+        ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, 0.1, 1, 0, FAKE, None, FAKE, 1 << 20,
+        None, 0, FAKE, 256, None) == A.ATTN_ERR_NULL
+    assert lib.attn_varlen_fwd_prescheduled(
+        ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 1, 0, FAKE, None, None, 0,
+        None, 0, FAKE, 256, None) == A.ATTN_ERR_WORKSPACE           # decode partials need it
+
+
 def test_default_partition_follows_the_batch_size():
     """partition_tokens 0: the longest of 16384 ... 256 keys that still gives at least 2048
     split workgroups (decodes x kv heads x head groups x partitions of max_seq_len), else 256

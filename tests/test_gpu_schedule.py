@@ -165,3 +165,92 @@ def test_decode_schedule_lists_every_partition_longest_first(window, part):
     assert all(a >= c for a, c in zip(costs, costs[1:])), costs   # longest first
     ref_out, ref_lse = oracle_on(b, q, kv, True, window)
     compare(out, lse, ref_out, ref_lse, label=f"decode schedule w{window} p{part}")
+
+
+# ---- decode schedule built ahead of the call (attn_build_decode_schedule) and read by
+# attn_varlen_fwd_prescheduled
+@pytest.mark.parametrize("window,part", [(0, 0), (0, 512), (3000, 0), (100, 1024)],
+                         ids=["default", "p512", "w3000", "w100-p1024"])
+def test_built_decode_schedule_equals_the_in_call_one(window, part):
+    nd = len(DECODE_LENS)
+    print(f"[case] built decode schedule window={window} partition={part}", flush=True)
+    b = gen.make_batch("decode-schedule", num_heads=8, num_kv_heads=2, head_size=64,
+                       block_size=16, dtype="bf16", query_lens=[1] * nd, seq_lens=DECODE_LENS,
+                       passes=[(True, window)], seed=92)
+    q, kv = gen.make_tensors(b, 92, DEV, poison=True)
+    desc = A.make_desc(num_seqs=nd, num_tokens=nd, num_decodes=nd, max_query_len=1,
+                       max_seq_len=b.max_seq_len, num_heads=8, num_kv_heads=2, head_size=64,
+                       num_blocks=b.num_blocks, block_size=16,
+                       max_blocks_per_seq=b.max_blocks_per_seq, dtype=A.ATTN_BF16,
+                       partition_tokens=part)
+    bt, qsl, sl = device_meta(b, DEV)
+    P = part or default_partition(nd, 8, 2, b.max_seq_len)
+    max_parts = -(-b.max_seq_len // P)
+    if window > 0:
+        max_parts = min(max_parts, -(-window // P) + 1)
+    assert A.attn_decode_schedule_bytes(desc, window) == -(-(4 * (1 + nd * max_parts)) // 256) * 256
+    sched = torch.full((A.attn_decode_schedule_bytes(desc, window) // 4,), -7, dtype=torch.int32,
+                       device=DEV)
+    A.attn_build_decode_schedule(desc, sl, window, sched)
+    ws = torch.zeros(A.attn_workspace_bytes(desc), dtype=torch.uint8, device=DEV)
+    out, out2 = torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty(nd, 8, dtype=torch.float32, device=DEV)
+    lse2 = torch.empty_like(lse)
+    A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl, b.scale, True, window, out, lse, ws)
+    torch.cuda.synchronize()
+    rows = nd * 8 * max_parts
+    off = -(-(rows * 64 + rows) * 4 // 256) * 256
+    s_call = ws[off:off + 4 * (1 + nd * max_parts)].view(torch.int32).cpu().numpy()
+    s_built = sched.cpu().numpy()
+    n = int(s_built[0])
+    assert n == int(s_call[0]) == len(oracle.decode_items(b.seq_lens, nd, window, P))
+    cost = {(r, p): c for r, p, c in oracle.decode_items(b.seq_lens, nd, window, P)}
+    listed = [(int(e) // max_parts, int(e) % max_parts) for e in s_built[1:1 + n]]
+    assert sorted(listed) == sorted(cost)
+    assert [cost[x] for x in listed] == [cost[(int(e) // max_parts, int(e) % max_parts)]
+                                         for e in s_call[1:1 + n]]       # same cost order
+    # the prescheduled call reads the built schedule and writes what the plain call wrote;
+    # a fresh workspace shows that it builds nothing there
+    ws2 = torch.zeros_like(ws)
+    A.attn_varlen_fwd_prescheduled(desc, q, kv, bt, qsl, sl, b.scale, True, window, out2, lse2,
+                                   ws2, decode_schedule=sched)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    assert not ws2[off:].any()
+
+
+def test_prescheduled_call_serves_several_layers_of_a_mixed_batch():
+    """Both schedules built once, three layer passes of the mixed GQA batch (decode rows +
+    prefill rows, window 300): each pass is bit-identical to the plain call and matches the
+    oracle; with only one of the two schedules the results are the same again."""
+    name, kw = BATCHES[1]
+    b, seed = _batch(name, kw)
+    window = 300
+    desc = _desc(b)
+    bt, qsl, sl = device_meta(b, DEV)
+    psched = torch.empty(A.attn_schedule_bytes(desc) // 4, dtype=torch.int32, device=DEV)
+    A.attn_build_schedule(desc, qsl, sl, True, window, psched)
+    dsched = torch.empty(A.attn_decode_schedule_bytes(desc, window) // 4, dtype=torch.int32,
+                         device=DEV)
+    A.attn_build_decode_schedule(desc, sl, window, dsched)
+    ws = torch.empty(A.attn_workspace_bytes(desc), dtype=torch.uint8, device=DEV)
+    for layer in range(3):
+        print(f"[case] prescheduled {name} layer {layer}", flush=True)
+        q = gen.make_q(b, seed, DEV, layer=layer)
+        kv = gen.make_kv(b, seed, DEV, layer=layer, poison=True)
+        res = []
+        for ps, ds in ((None, None), (psched, dsched), (psched, None), (None, dsched)):
+            out = torch.empty_like(q)
+            lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=DEV)
+            if ps is None and ds is None:
+                A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl, b.scale, True, window, out, lse, ws)
+            else:
+                A.attn_varlen_fwd_prescheduled(desc, q, kv, bt, qsl, sl, b.scale, True, window,
+                                               out, lse, ws, prefill_schedule=ps,
+                                               decode_schedule=ds)
+            res.append((out, lse))
+        torch.cuda.synchronize()
+        for out, lse in res[1:]:
+            assert torch.equal(out, res[0][0]) and torch.equal(lse, res[0][1])
+        ref_out, ref_lse = oracle_on(b, q, kv, True, window)
+        compare(res[1][0], res[1][1], ref_out, ref_lse, label=f"layer {layer}")
