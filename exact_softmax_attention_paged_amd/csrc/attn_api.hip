@@ -103,12 +103,23 @@ int64_t decode_max_parts(const attn_desc* d, int32_t window) {
   return n < 1 ? 1 : n;
 }
 
-// Split-KV workspace: the partitions' fp32 results ([num_decodes][Hq][max_parts][d], then
-// [num_decodes][Hq][max_parts] log-sum-exps), then, from a 256-byte boundary, the decode
+// Decode work items (segments) a request may span, capped for a window like the partitions.
+int64_t decode_max_segs(const attn_desc* d, int32_t window) {
+  const int64_t S = attn::decode_segment_tokens(partition_tokens(d));
+  int64_t n = ceil_div(d->max_seq_len, S);
+  if (window > 0) {
+    const int64_t wn = ceil_div(window, S) + 1;
+    if (wn < n) n = wn;
+  }
+  return n < 1 ? 1 : n;
+}
+
+// Split-KV workspace: the partitions' results ([num_decodes][Hq][max_parts][d] bf16, then
+// [num_decodes][Hq][max_parts] fp32 log-sum-exps), then, from a 256-byte boundary, the decode
 // schedule region (below).
 int64_t decode_results_bytes(const attn_desc* d, int64_t max_parts) {
   const int64_t rows = (int64_t)d->num_decodes * d->num_heads * max_parts;
-  return ceil_div((rows * d->head_size + rows) * 4, 256) * 256;
+  return ceil_div(rows * d->head_size * 2 + rows * 4, 256) * 256;
 }
 // Decode schedule region: the item count, then one int32 per (request, partition) slot.
 int64_t decode_schedule_ints(const attn_desc* d, int64_t max_parts) {
@@ -189,8 +200,9 @@ attn::DecodeParams decode_params(const attn_desc& d, const attn::PrefillParams& 
   dp.seq_lens = pp.seq_lens;
   dp.out = pp.out;
   dp.lse = pp.lse;
-  dp.ws_o = ws;
-  dp.ws_lse = ws + (int64_t)d.num_decodes * d.num_heads * max_parts * d.head_size;
+  const int64_t rows = (int64_t)d.num_decodes * d.num_heads * max_parts;
+  dp.ws_o = reinterpret_cast<__bf16*>(ws);
+  dp.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + rows * d.head_size * 2);
   dp.v_offset = pp.v_offset;
   dp.num_heads = d.num_heads;
   dp.num_kv_heads = d.num_kv_heads;
@@ -200,6 +212,8 @@ attn::DecodeParams decode_params(const attn_desc& d, const attn::PrefillParams& 
   dp.num_decodes = d.num_decodes;
   dp.part_tokens = partition_tokens(&d);
   dp.max_parts = (int32_t)max_parts;
+  dp.seg_tokens = attn::decode_segment_tokens(dp.part_tokens);
+  dp.max_segs = (int32_t)decode_max_segs(&d, pp.window);
   dp.schedule = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
                                            decode_results_bytes(&d, max_parts));
   dp.window = pp.window;
@@ -525,8 +539,8 @@ attn_status attn_build_decode_schedule(const attn_desc* desc, const int32_t* seq
   sp.seq_lens = seq_lens;
   sp.schedule = schedule;
   sp.num_decodes = desc->num_decodes;
-  sp.part_tokens = partition_tokens(desc);
-  sp.max_parts = (int32_t)decode_max_parts(desc, window);
+  sp.part_tokens = attn::decode_segment_tokens(partition_tokens(desc));
+  sp.max_parts = (int32_t)decode_max_segs(desc, window);
   sp.window = window > 0 ? window : 0;
   sp.kv_skip_keys = 0;
   return attn::launch_decode_schedule(sp, static_cast<hipStream_t>(stream)) == hipSuccess

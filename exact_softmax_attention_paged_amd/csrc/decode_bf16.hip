@@ -5,9 +5,12 @@
 // softmax. Here one unit of work is one (decode request, kv head, partition of part_tokens
 // keys) with all q heads that share that kv head (num_queries_per_kv of the vLLM
 // FlashAttention page's FlashAttentionImpl section), so every K/V byte is read from HBM once
-// per kv head. The partition result (normalised output and its lse) goes to the workspace,
-// and a second kernel merges the partitions of each (request, q head) through their
-// log-sum-exp. A request whose visible keys fit one partition is written directly.
+// per kv head. The partition result goes to the workspace - the normalised output rounded to
+// bf16 (a convex combination of V rows, so the rounding adds at most 2^-9 of its magnitude,
+// as the bf16 output itself does; writing fp32 there cost ~8 % of the decode time at 512-key
+// partitions, writes being dear in a read-saturated stream) and its log-sum-exp in fp32 - and
+// a second kernel merges the partitions of each (request, q head) through their log-sum-exp
+// in fp32. A request whose visible keys fit one partition is written directly.
 //
 // A unit runs on one wave (partitions of up to 1024 keys) or on a 4-wave workgroup whose
 // waves take a quarter of the partition each and combine through LDS (longer partitions).
@@ -26,10 +29,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kChunk = 32;       // keys per wave iteration
-// Partitions of at most this many keys run one per wave (decode_wave_kernel), longer ones one
-// per workgroup (decode_split_kernel). With block_size >= 16 a partition of 1024 keys spans
-// at most 64 blocks, one per lane.
-constexpr int kWavePartMax = 1024;
 
 // 8 E4M3 codes (two 32-bit words) -> 8 bf16 values, exactly (every E4M3 value is a bf16
 // value; v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts two codes, checked on gfx950 for all
@@ -90,12 +89,12 @@ struct WaveTiles {
 //     columns);
 //   * V rows are copied into the wave's LDS tile and read back transposed with
 //     ds_read_b64_tr_b16 as the A operand of O^T += V^T . P^T.
-template <int D, bool FP8, class BlockOf>
+template <int D, bool FP8, class BlockOf, class After>
 __device__ __forceinline__ void stream_keys(const DecodeParams& p, int kvh,
                                             const bf16x8 (&qf)[D / 32], int c_base, int w_begin,
                                             int w_end, int last_key, BlockOf block_of,
                                             __bf16* sVw, __bf16* sKw, float& m_run,
-                                            float& l_run, floatx4 (&o)[D / 16]) {
+                                            float& l_run, floatx4 (&o)[D / 16], After after) {
   using T = WaveTiles<D>;
   constexpr int RS = T::RS;
   constexpr int KRS = T::KRS;
@@ -182,7 +181,11 @@ __device__ __forceinline__ void stream_keys(const DecodeParams& p, int kvh,
   for (int dc = 0; dc < DC; ++dc) o[dc] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // consume chunk ci held in ch; after its QK^T MFMAs, refill ch with chunk ci + 2
-  auto consume = [&](Chunk& ch, int ci) __attribute__((always_inline)) {
+  // Refill (a std::integral_constant<bool, ...>): whether ch is refilled; kept a compile-time
+  // choice so that every load in the main loop is unconditional and the compiler's wait
+  // counts see a fixed number of loads in flight (a refill under a run-time condition made
+  // it wait for both buffers before each chunk, leaving one chunk in flight instead of two)
+  auto consume = [&](Chunk& ch, int ci, auto refill) __attribute__((always_inline)) {
     const int kb = c_base + (c_first + ci) * kChunk;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -202,7 +205,7 @@ __device__ __forceinline__ void stream_keys(const DecodeParams& p, int kvh,
         *reinterpret_cast<bf16x8*>(&sKw[(j * RPI + v_row) * KRS + EPL * v_chunk]) =
             __builtin_bit_cast(bf16x8, ch.k[j / KW][j % KW]);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the writes land before any read
-      if (ci + kInFlight < n_chunks) load_chunk(ch, kb + kInFlight * kChunk);
+      if constexpr (decltype(refill)::value) load_chunk(ch, kb + kInFlight * kChunk);
     }
     floatx4 sc[2];
 #pragma unroll
@@ -220,7 +223,7 @@ __device__ __forceinline__ void stream_keys(const DecodeParams& p, int kvh,
       sc[t2] = acc;
     }
     if constexpr (FP8) {
-      if (ci + kInFlight < n_chunks) load_chunk(ch, kb + kInFlight * kChunk);
+      if constexpr (decltype(refill)::value) load_chunk(ch, kb + kInFlight * kChunk);
     }
     if (kb < w_begin || kb + kChunk > w_end) {
 #pragma unroll
@@ -265,36 +268,50 @@ __device__ __forceinline__ void stream_keys(const DecodeParams& p, int kvh,
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
 
-  // kInFlight chunks in flight per wave (4 for E4M3 measured no faster than 2)
+  // kInFlight = 2 chunks in flight per wave (4 for E4M3 measured no faster than 2). The chunk
+  // count is rounded up to even: the extra chunk lies past w_end (clamped loads, masked
+  // scores), so every pair of chunks is one pass of the loop with both refills issued; the
+  // last pair refills nothing.
+  static_assert(kInFlight == 2, "the loop below consumes chunks in pairs");
+  if (n_chunks == 0) return;
+  const int n_pairs = (n_chunks + 1) / 2;
+  const int k0 = c_base + c_first * kChunk;
+  auto after_real = [&](int ci) __attribute__((always_inline)) {
+    if (ci < n_chunks) after(k0 + ci * kChunk);
+  };
   Chunk buf[kInFlight];
-#pragma unroll
-  for (int b = 0; b < kInFlight; ++b)
-    if (b < n_chunks) load_chunk(buf[b], c_base + (c_first + b) * kChunk);
-  for (int ci = 0; ci < n_chunks; ci += kInFlight) {
-#pragma unroll
-    for (int b = 0; b < kInFlight; ++b)
-      if (ci + b < n_chunks) consume(buf[b], ci + b);
+  load_chunk(buf[0], k0);
+  load_chunk(buf[1], k0 + kChunk);
+  for (int pr = 0; pr + 1 < n_pairs; ++pr) {
+    consume(buf[0], 2 * pr, std::true_type{});
+    after_real(2 * pr);
+    consume(buf[1], 2 * pr + 1, std::true_type{});
+    after_real(2 * pr + 1);
   }
+  consume(buf[0], 2 * n_pairs - 2, std::false_type{});
+  after_real(2 * n_pairs - 2);
+  consume(buf[1], 2 * n_pairs - 1, std::false_type{});
+  after_real(2 * n_pairs - 1);
 }
 
 // The decode work item in schedule slot `slot` for (kv head, head group) `hw`, and the keys it
 // reads. valid is false for slots past the item count.
 struct DecodeItem {
   bool valid;
-  int r, pi, hw, kvh, nh, h0, tok;
-  int nparts;                    // partitions of the request holding visible keys
-  int p_start, k_begin, k_end;   // partition start, visible keys [k_begin, k_end)
+  int r, hw, kvh, nh, h0, tok;
+  int first_part, nparts;        // the request's partitions holding visible keys
+  int p_start, k_begin, k_end;   // segment start, its visible keys [k_begin, k_end)
 };
 __device__ __forceinline__ DecodeItem decode_item(const DecodeParams& p, int slot, int hw) {
   DecodeItem it{};
   const int group = p.num_heads / p.num_kv_heads;
   const int head_groups = (group + 15) / 16;
   const int count = p.items[0];
-  const int item = p.items[1 + min(slot, p.num_decodes * p.max_parts - 1)];
+  const int item = p.items[1 + min(slot, p.num_decodes * p.max_segs - 1)];
   it.valid = slot < count;
   if (!it.valid) return it;
-  it.r = item / p.max_parts;
-  it.pi = item % p.max_parts;
+  it.r = item / p.max_segs;
+  const int si = item % p.max_segs;
   it.hw = hw;
   it.kvh = hw / head_groups;
   const int hg = hw % head_groups;
@@ -302,13 +319,14 @@ __device__ __forceinline__ DecodeItem decode_item(const DecodeParams& p, int slo
   it.h0 = it.kvh * group + hg * 16;                   // first q head
   // keys of this pass: [0, sl) after skipping kv_skip_blocks leading blocks
   const int sl = p.seq_lens[it.r] - p.kv_skip_blocks * p.block_size;
-  int first;
-  decode_partitions(sl, p.window, p.part_tokens, &first, &it.nparts);
+  int first_seg, nsegs;
+  decode_partitions(sl, p.window, p.seg_tokens, &first_seg, &nsegs);
+  decode_partitions(sl, p.window, p.part_tokens, &it.first_part, &it.nparts);
   it.nparts = min(it.nparts, p.max_parts);   // only reachable with seq_len > max_seq_len
-  it.p_start = (first + it.pi) * p.part_tokens;
+  it.p_start = (first_seg + si) * p.seg_tokens;
   const int lo = p.window > 0 ? max(0, sl - p.window) : 0;
   it.k_begin = max(lo, it.p_start);
-  it.k_end = min(sl, it.p_start + p.part_tokens);
+  it.k_end = min(sl, it.p_start + p.seg_tokens);
   it.tok = p.qsl[it.r];
   return it;
 }
@@ -316,9 +334,9 @@ __device__ __forceinline__ DecodeItem decode_item(const DecodeParams& p, int slo
 // FP8 = true: the cache holds E4M3 codes (one byte per element) with per-tensor scales; the
 // host folds k_scale into p.scale and the kernel multiplies the output by p.v_scale.
 //
-// Workgroup mode (partitions of more than kWavePartMax keys): one workgroup of 4 waves per
-// (item, kv head, head group); each wave streams its own quarter of the partition and the 4
-// waves' (max, sum, O) are combined through LDS at the end.
+// Workgroup mode (partitions of more than kWaveSegmentTokens keys, one per segment): one
+// workgroup of 4 waves per (item, kv head, head group); each wave streams its own quarter of
+// the partition and the 4 waves' (max, sum, O) are combined through LDS at the end.
 template <int D, bool FP8>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams p) {
   using T = WaveTiles<D>;
@@ -371,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
                       [&](uint32_t bidx) __attribute__((always_inline)) {
                         return sBlk[bidx - b_first];
                       },
-                      sVw, sKw, m_run, l_run, o);
+                      sVw, sKw, m_run, l_run, o, [](int) {});
 
   // ---- combine the 4 waves: (m, l, O^T) -> partition result
   const float c_log2 = p.scale * kLog2e;
@@ -419,20 +437,23 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const DecodeParams
     for (int x = 0; x < DPT; ++x) dst[x] = to_bf16(acc[x]);
     if (p.lse != nullptr && d0 == 0) p.lse[(int64_t)it.tok * p.num_heads + hq] = lse_part;
   } else {
-    const int64_t slot = ((int64_t)it.r * p.num_heads + hq) * p.max_parts + it.pi;
-    float* dst = p.ws_o + slot * D + d0;
+    const int pi = it.k_begin / p.part_tokens - it.first_part;   // the segment's partition
+    const int64_t slot = ((int64_t)it.r * p.num_heads + hq) * p.max_parts + pi;
+    __bf16* dst = p.ws_o + slot * D + d0;
 #pragma unroll
-    for (int x = 0; x < DPT; x += 4)
-      *reinterpret_cast<floatx4*>(dst + x) = floatx4{acc[x], acc[x + 1], acc[x + 2], acc[x + 3]};
+    for (int x = 0; x < DPT; ++x) dst[x] = to_bf16(acc[x]);
     if (d0 == 0) p.ws_lse[slot] = lse_part;
   }
 }
 
-// Wave mode (partitions of at most kWavePartMax keys): each wave of a 4-wave workgroup is one
-// (item, kv head, head group) unit and streams the whole partition alone, so no cross-wave
-// combine and no barrier; the partition's block ids (at most 64) sit one per lane and reach
-// the address computation through v_readlane. Units are numbered like the workgroup mode's
-// grid (item slot * heads_wg + (kv head, head group)), 4 consecutive units per workgroup.
+// Wave mode (partitions of at most kWaveSegmentTokens keys): each wave of a 4-wave workgroup
+// is one (item, kv head, head group) unit and streams the item's whole segment alone (no
+// cross-wave combine, no barrier), writing one result per partition of the segment as its
+// last chunk is consumed: a segment of several short partitions pays the unit's start-up
+// (schedule slot, block ids, Q^T, the first loads) once. The segment's block ids (at most 64)
+// sit one per lane and reach the address computation through v_readlane. Units are numbered
+// like the workgroup mode's grid (item slot * heads_wg + (kv head, head group)), 4 consecutive
+// units per workgroup.
 template <int D, bool FP8>
 __global__ __launch_bounds__(256, 2) void decode_wave_kernel(const DecodeParams p) {
   using T = WaveTiles<D>;
@@ -448,8 +469,8 @@ __global__ __launch_bounds__(256, 2) void decode_wave_kernel(const DecodeParams 
   const DecodeItem it = decode_item(p, unit / heads_wg, unit % heads_wg);
   if (!it.valid) return;
 
-  // lane i holds the cache block of the partition's i-th block (n_blk <= 64: the partition
-  // has at most kWavePartMax keys and block_size is a multiple of 16)
+  // lane i holds the cache block of the segment's i-th block (n_blk <= 64: the segment has at
+  // most kWaveSegmentTokens keys and block_size is a multiple of 16)
   const int b_first = it.p_start / p.block_size;
   const int n_blk = (it.k_end - 1) / p.block_size - b_first + 1;
   const int32_t* __restrict__ bt =
@@ -461,37 +482,54 @@ __global__ __launch_bounds__(256, 2) void decode_wave_kernel(const DecodeParams 
 
   float m_run, l_run;
   floatx4 o[D / 16];
+  // after the chunk at key kb: at the end of a partition (or of the segment), its result
+  // goes out (lane (G, li) holds O^T rows d = 16 dc + 4 G .. +3 of q head h0 + li) and the
+  // state restarts for the next partition
+  auto after = [&](int kb) __attribute__((always_inline)) {
+    const int k_next = kb + kChunk;
+    if (k_next % p.part_tokens != 0 && k_next < it.k_end) return;
+    const int pi = kb / p.part_tokens - it.first_part;
+    const float l = column_sum(l_run);
+    const float inv = l > 0.f ? (FP8 ? p.v_scale : 1.f) / l : 0.f;
+    const float lse_part = l > 0.f ? p.scale * m_run + __logf(l) : -INFINITY;
+    const int hq = it.h0 + li;
+    if (li < it.nh) {
+      if (it.nparts == 1 && p.pre_o == nullptr) {
+        __bf16* dst = static_cast<__bf16*>(p.out) + ((int64_t)it.tok * p.num_heads + hq) * D;
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) {
+          const floatx4 v = o[dc] * inv;
+          bf16x4 b4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b4[e] = to_bf16(v[e]);
+          *reinterpret_cast<bf16x4*>(dst + 16 * dc + 4 * G) = b4;
+        }
+        if (p.lse != nullptr && G == 0) p.lse[(int64_t)it.tok * p.num_heads + hq] = lse_part;
+      } else if (pi < p.max_parts) {   // only false with seq_len > max_seq_len
+        const int64_t slot = ((int64_t)it.r * p.num_heads + hq) * p.max_parts + pi;
+        __bf16* dst = p.ws_o + slot * D;
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) {
+          const floatx4 v = o[dc] * inv;
+          bf16x4 b4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b4[e] = to_bf16(v[e]);
+          *reinterpret_cast<bf16x4*>(dst + 16 * dc + 4 * G) = b4;
+        }
+        if (G == 0) p.ws_lse[slot] = lse_part;
+      }
+    }
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) o[dc] = floatx4{0.f, 0.f, 0.f, 0.f};
+  };
   stream_keys<D, FP8>(p, it.kvh, qf, it.p_start, it.k_begin, it.k_end, it.k_end - 1,
                       [&](uint32_t bidx) __attribute__((always_inline)) {
                         return __builtin_amdgcn_readlane(blk_lane, (int)(bidx - b_first));
                       },
-                      sV + w * T::V_TILE, sK + (FP8 ? 0 : w * T::K_TILE), m_run, l_run, o);
-
-  // lane (G, li) holds O^T rows d = 16 dc + 4 G .. +3 of q head h0 + li
-  const float l = column_sum(l_run);
-  if (li >= it.nh) return;
-  const float inv = l > 0.f ? (FP8 ? p.v_scale : 1.f) / l : 0.f;
-  const float lse_part = l > 0.f ? p.scale * m_run + __logf(l) : -INFINITY;
-  const int hq = it.h0 + li;
-  if (it.nparts == 1 && p.pre_o == nullptr) {
-    __bf16* dst = static_cast<__bf16*>(p.out) + ((int64_t)it.tok * p.num_heads + hq) * D;
-#pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) {
-      const floatx4 v = o[dc] * inv;
-      bf16x4 b4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) b4[e] = to_bf16(v[e]);
-      *reinterpret_cast<bf16x4*>(dst + 16 * dc + 4 * G) = b4;
-    }
-    if (p.lse != nullptr && G == 0) p.lse[(int64_t)it.tok * p.num_heads + hq] = lse_part;
-  } else {
-    const int64_t slot = ((int64_t)it.r * p.num_heads + hq) * p.max_parts + it.pi;
-    float* dst = p.ws_o + slot * D;
-#pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc)
-      *reinterpret_cast<floatx4*>(dst + 16 * dc + 4 * G) = o[dc] * inv;
-    if (G == 0) p.ws_lse[slot] = lse_part;
-  }
+                      sV + w * T::V_TILE, sK + (FP8 ? 0 : w * T::K_TILE), m_run, l_run, o,
+                      after);
 }
 
 // One wave per (q head, decode request): out = sum_p exp(lse_p - L) o_p and lse = L =
@@ -535,7 +573,7 @@ __global__ __launch_bounds__(64) void lse_merge_kernel(const DecodeParams p) {
       const int64_t slot = base + min(p0 + i, nparts - 1);   // past the end: masked below
       l[i] = p.ws_lse[slot];
 #pragma unroll
-      for (int x = 0; x < DPL; ++x) v[i][x] = p.ws_o[slot * D + lane + kWave * x];
+      for (int x = 0; x < DPL; ++x) v[i][x] = (float)p.ws_o[slot * D + lane + kWave * x];
     }
     float mb = m;
 #pragma unroll
@@ -575,16 +613,16 @@ hipError_t launch(const DecodeParams& p, hipStream_t stream) {
     sp.seq_lens = p.seq_lens;
     sp.schedule = p.schedule;
     sp.num_decodes = p.num_decodes;
-    sp.part_tokens = p.part_tokens;
-    sp.max_parts = p.max_parts;
+    sp.part_tokens = p.seg_tokens;
+    sp.max_parts = p.max_segs;
     sp.window = p.window;
     sp.kv_skip_keys = p.kv_skip_blocks * p.block_size;
     const hipError_t e = launch_decode_schedule(sp, stream);
     if (e != hipSuccess) return e;
     pk.items = p.schedule;
   }
-  const int64_t units = (int64_t)p.num_decodes * p.max_parts * p.num_kv_heads * head_groups;
-  if (p.part_tokens <= kWavePartMax)
+  const int64_t units = (int64_t)p.num_decodes * p.max_segs * p.num_kv_heads * head_groups;
+  if (p.part_tokens <= kWaveSegmentTokens)
     hipLaunchKernelGGL((decode_wave_kernel<D, FP8>), dim3((unsigned)((units + kWaves - 1) / kWaves)),
                        dim3(256), 0, stream, pk);
   else

@@ -9,6 +9,16 @@ namespace attn {
 // kMaxPartitionTokens / 16 entries).
 constexpr int32_t kMaxPartitionTokens = 16384;
 
+// Keys of one decode work item (a segment of a request's keys). Partitions of up to
+// kWaveSegmentTokens keys are streamed by one wave each, as many whole partitions per item as
+// fit in kWaveSegmentTokens keys (the wave writes one partial result per partition); a longer
+// partition is one item, streamed by one workgroup.
+constexpr int32_t kWaveSegmentTokens = 1024;
+__host__ __device__ inline int32_t decode_segment_tokens(int32_t part_tokens) {
+  return part_tokens <= kWaveSegmentTokens ? kWaveSegmentTokens / part_tokens * part_tokens
+                                           : part_tokens;
+}
+
 // One prefill launch covers requests [seq_begin, seq_begin + num_seqs) and every q head.
 struct PrefillParams {
   const void* q;                // [num_tokens][num_heads][head_size]
@@ -55,11 +65,14 @@ struct DecodeParams {
   const int32_t* seq_lens;
   void* out;
   float* lse;
-  float* ws_o;                  // [num_decodes][num_heads][max_parts][head_size]
-  float* ws_lse;                // [num_decodes][num_heads][max_parts]
+  __bf16* ws_o;                 // [num_decodes][num_heads][max_parts][head_size] partition
+                                // results, normalised, rounded to bf16
+  float* ws_lse;                // [num_decodes][num_heads][max_parts] their log-sum-exps
   int64_t v_offset;
   int32_t num_heads, num_kv_heads, head_size, block_size, max_blocks;
   int32_t num_decodes, part_tokens, max_parts;  // max_parts: partitions a request may span
+  int32_t seg_tokens, max_segs; // work items: segments of decode_segment_tokens(part_tokens)
+                                // keys; max_segs: segments a request may span
   int32_t window;
   float scale;
   uint64_t group_recip;         // ceil(2^32 / (block_size / 16)), as in PrefillParams
@@ -67,9 +80,10 @@ struct DecodeParams {
                                 // into scale by the host)
   int32_t* schedule;            // where the launch builds this call's work items (see
                                 // DecodeScheduleParams), unless items is set
-  const int32_t* items;         // the items the split kernel reads, longest first: schedule,
-                                // or a schedule the caller built ahead (then nothing is built);
-                                // unit = item slot * (num_kv_heads * head groups) + kv head group
+  const int32_t* items;         // the (request, segment) items the split kernel reads, longest
+                                // first: schedule, or a schedule the caller built ahead (then
+                                // nothing is built); unit = item slot * (num_kv_heads * head
+                                // groups) + kv head group
   // Cascade suffix pass (zero / null for a plain call):
   int32_t kv_skip_blocks;       // as in PrefillParams
   const float* pre_o;           // non-null: a partial result over the prefix, fp32
@@ -125,10 +139,11 @@ struct ScheduleParams {
   int32_t causal, window;
 };
 
-// Decode work schedule: items (decode request r, partition pi) coded r * max_parts + pi, for
-// every partition holding visible keys, sorted by their number of keys (in 16-key units),
-// longest first, so the in-order workgroup dispatch leaves the short partitions to the end of
-// the grid. schedule[0] = item count, schedule[1 + i] = item i.
+// Decode work schedule: items (decode request r, key range pi of part_tokens keys) coded
+// r * max_parts + pi, for every range holding visible keys, sorted by their number of keys (in
+// 16-key units), longest first, so the in-order workgroup dispatch leaves the short ranges to
+// the end of the grid. schedule[0] = item count, schedule[1 + i] = item i. The decode kernel's
+// items are its segments (part_tokens = its segment length, max_parts = its max_segs).
 struct DecodeScheduleParams {
   const int32_t* seq_lens;
   int32_t* schedule;

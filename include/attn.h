@@ -90,9 +90,9 @@ typedef struct attn_desc {
 
 /*
  * attn_workspace_bytes: device workspace that attn_varlen_fwd needs for `desc`.
- * It holds the per-partition partial outputs and log-sum-exps of the decode rows
- * ([RBLN] Overview: partition results combined by online softmax):
- *   num_decodes * num_heads * P * (head_size + 1) * 4 bytes, rounded up to 256,
+ * It holds the per-partition partial outputs (normalised, bf16) and log-sum-exps (fp32) of
+ * the decode rows ([RBLN] Overview: partition results combined by online softmax):
+ *   num_decodes * num_heads * P * (head_size * 2 + 4) bytes, rounded up to 256,
  * where P is the number of partitions of max_seq_len (capped for a window in
  * attn_varlen_fwd), followed by the decode work schedule the call builds there:
  *   (1 + num_decodes * P) * 4 bytes, rounded up to 256.
@@ -355,12 +355,16 @@ attn_status attn_varlen_fwd_scheduled(const attn_desc* desc, const void* q, cons
  * Decode work schedule built ahead of the attention call (the same [FA] FA3 reasoning as the
  * prefill schedule above, applied to the split-KV decode rows whose partitions [RBLN] Overview
  * combines by online softmax). attn_varlen_fwd builds this schedule in its workspace on every
- * call with one small kernel: the (decode request, partition) items that hold visible keys,
- * sorted by the number of keys each reads, longest first. It depends only on seq_lens, the
- * window and the partition length, so a batch builds it once and every layer reuses it.
+ * call with one small kernel: the (decode request, segment) items that hold visible keys,
+ * sorted by the number of keys each reads, longest first. A segment is one partition, or, for
+ * partitions of at most 1024 keys, floor(1024 / partition_tokens) consecutive partitions (one
+ * wave streams them and writes one partial result per partition). The schedule depends only
+ * on seq_lens, the window and the partition length, so a batch builds it once and every layer
+ * reuses it.
  *
  * attn_decode_schedule_bytes: bytes of the decode schedule buffer for `window`: the schedule
- *   region of attn_workspace_bytes with P capped for the window; 0 when the call has no
+ *   region of attn_workspace_bytes with P capped for the window (room for one item per
+ *   partition, at least one per segment); 0 when the call has no
  *   split-KV decode rows (num_decodes == 0 or dtype ATTN_F32). Errors: ATTN_ERR_NULL and the
  *   descriptor errors of attn_workspace_bytes.
  * attn_build_decode_schedule: queue the kernel that writes the decode schedule (int32; element

@@ -108,7 +108,7 @@ def test_workspace_size_and_check():
     parts = -(-40 // 2048)                     # the default partition length
 
     def expected(decodes, parts):              # partition results, then the work schedule
-        return (-(-(decodes * 8 * parts * 129 * 4) // 256) * 256 +
+        return (-(-(decodes * 8 * parts * (128 * 2 + 4)) // 256) * 256 +
                 -(-((1 + decodes * parts) * 4) // 256) * 256)
     assert need == expected(1, parts)
     assert _fwd(d, ws=None, ws_bytes=0) == A.ATTN_ERR_WORKSPACE
@@ -387,7 +387,7 @@ def test_default_partition_follows_the_batch_size():
         return A.attn_workspace_bytes(d)
 
     def expected(decodes, parts, heads=32, d=128):
-        return (-(-(decodes * heads * parts * (d + 1) * 4) // 256) * 256 +
+        return (-(-(decodes * heads * parts * (d * 2 + 4)) // 256) * 256 +
                 -(-((1 + decodes * parts) * 4) // 256) * 256)
     # 256 requests x 8 kv heads = 2048 workgroups with one 16384-key partition each
     assert need(256, 8192) == expected(256, 1)

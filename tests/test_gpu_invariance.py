@@ -106,10 +106,12 @@ def test_two_eager_calls_are_bitwise_equal(causal, window):
 # The tolerance of the partition comparisons. Each result rounds its probabilities to bf16
 # against its own running maximum (that of a partition, of a wave's share of it, or of the whole
 # row) before the P.V product, so a weight may carry a different rounding (up to 2^-9 relative)
-# in the two results, and the final bf16 rounding of two nearby fp32 values may differ by one
-# unit (2^-8 relative). On this batch that is at most one bf16 unit of an output below 0.25
-# (2^-10) and a mean of 2-5e-5 on every partition length (measured on gfx950); the bounds below
-# leave 4x margin on each. The lse is formed in fp32 from the same scores on both sides (only
+# in the two results; a split row also stores each partition's normalised result in bf16
+# before the merge (at most 2^-9 of that partition result's magnitude, and the merge weights
+# sum to 1); and the final bf16 rounding of two nearby fp32 values may differ by one unit
+# (2^-8 relative). On this batch that is at most one bf16 unit of an output below 0.25 (2^-10)
+# and a mean of 3-7e-5 on every partition length (measured on gfx950); the bounds below leave
+# 3-4x margin on each. The lse is formed in fp32 from the same scores on both sides (only
 # the order of the partial sums and the reference maxima differ): measured 1-2e-6, bound 1e-5.
 PART_OUT_MAX, PART_OUT_MEAN, PART_LSE_MAX = 4e-3, 2e-4, 1e-5
 

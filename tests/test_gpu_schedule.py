@@ -116,6 +116,18 @@ DECODE_LENS = [1, 15, 16, 17, 511, 512, 513, 2047, 2048, 2049, 4095, 4096, 4097,
                300, 7777, 12345]
 
 
+def segment(P):
+    """Keys of one decode work item for partition length P (include/attn.h): a partition of
+    up to 1024 keys is streamed by one wave, as many whole partitions per item as fit in 1024
+    keys; a longer partition is one item."""
+    return 1024 // P * P if P <= 1024 else P
+
+
+def capped(n_keys, P, window):
+    n = -(-n_keys // P)
+    return min(n, -(-window // P) + 1) if window > 0 else n
+
+
 def default_partition(num_decodes, num_heads, num_kv_heads, max_seq_len):
     """The library's partition length for partition_tokens = 0 (include/attn.h): the longest
     of 16384, 8192, ..., 256 giving at least 2048 split workgroups, else 256."""
@@ -128,7 +140,7 @@ def default_partition(num_decodes, num_heads, num_kv_heads, max_seq_len):
 
 @pytest.mark.parametrize("window,part", [(0, 0), (0, 512), (3000, 0), (100, 1024)],
                          ids=["default", "p512", "w3000", "w100-p1024"])
-def test_decode_schedule_lists_every_partition_longest_first(window, part):
+def test_decode_schedule_lists_every_segment_longest_first(window, part):
     nd = len(DECODE_LENS)
     print(f"[case] decode schedule window={window} partition={part}", flush=True)
     b = gen.make_batch("decode-schedule", num_heads=8, num_kv_heads=2, head_size=64,
@@ -146,20 +158,21 @@ def test_decode_schedule_lists_every_partition_longest_first(window, part):
     lse = torch.empty(nd, 8, dtype=torch.float32, device=DEV)
     A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl, b.scale, True, window, out, lse, ws)
     torch.cuda.synchronize()
-    # workspace layout of the C layer: partition results ([nd][Hq][max_parts][d] and
-    # [nd][Hq][max_parts] fp32, padded to 256 bytes), then the schedule
+    # workspace layout of the C layer: partition results ([nd][Hq][max_parts][d] bf16 and
+    # [nd][Hq][max_parts] fp32, padded to 256 bytes), then the schedule of the work items:
+    # (request, segment) pairs, a segment being segment(P) keys
     P = part or default_partition(nd, 8, 2, b.max_seq_len)
-    max_parts = -(-b.max_seq_len // P)
-    if window > 0:
-        max_parts = min(max_parts, -(-window // P) + 1)
+    max_parts = capped(b.max_seq_len, P, window)
+    S = segment(P)
+    max_segs = capped(b.max_seq_len, S, window)
     rows = nd * 8 * max_parts
-    off = -(-(rows * 64 + rows) * 4 // 256) * 256
-    s = ws[off:off + 4 * (1 + nd * max_parts)].view(torch.int32).cpu().numpy()
-    items = oracle.decode_items(b.seq_lens, nd, window, P)
+    off = -(-(rows * 64 * 2 + rows * 4) // 256) * 256
+    s = ws[off:off + 4 * (1 + nd * max_segs)].view(torch.int32).cpu().numpy()
+    items = oracle.decode_items(b.seq_lens, nd, window, S)
     cost = {(r, p): c for r, p, c in items}
     n = int(s[0])
     assert n == len(items)
-    listed = [(int(e) // max_parts, int(e) % max_parts) for e in s[1:1 + n]]
+    listed = [(int(e) // max_segs, int(e) % max_segs) for e in s[1:1 + n]]
     assert sorted(listed) == sorted(cost)                     # every partition exactly once
     costs = [cost[x] for x in listed]
     assert all(a >= c for a, c in zip(costs, costs[1:])), costs   # longest first
@@ -185,9 +198,10 @@ def test_built_decode_schedule_equals_the_in_call_one(window, part):
                        partition_tokens=part)
     bt, qsl, sl = device_meta(b, DEV)
     P = part or default_partition(nd, 8, 2, b.max_seq_len)
-    max_parts = -(-b.max_seq_len // P)
-    if window > 0:
-        max_parts = min(max_parts, -(-window // P) + 1)
+    max_parts = capped(b.max_seq_len, P, window)
+    S = segment(P)
+    max_segs = capped(b.max_seq_len, S, window)
+    # sized for one item per partition (at least one per segment)
     assert A.attn_decode_schedule_bytes(desc, window) == -(-(4 * (1 + nd * max_parts)) // 256) * 256
     sched = torch.full((A.attn_decode_schedule_bytes(desc, window) // 4,), -7, dtype=torch.int32,
                        device=DEV)
@@ -199,15 +213,15 @@ def test_built_decode_schedule_equals_the_in_call_one(window, part):
     A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl, b.scale, True, window, out, lse, ws)
     torch.cuda.synchronize()
     rows = nd * 8 * max_parts
-    off = -(-(rows * 64 + rows) * 4 // 256) * 256
-    s_call = ws[off:off + 4 * (1 + nd * max_parts)].view(torch.int32).cpu().numpy()
+    off = -(-(rows * 64 * 2 + rows * 4) // 256) * 256
+    s_call = ws[off:off + 4 * (1 + nd * max_segs)].view(torch.int32).cpu().numpy()
     s_built = sched.cpu().numpy()
     n = int(s_built[0])
-    assert n == int(s_call[0]) == len(oracle.decode_items(b.seq_lens, nd, window, P))
-    cost = {(r, p): c for r, p, c in oracle.decode_items(b.seq_lens, nd, window, P)}
-    listed = [(int(e) // max_parts, int(e) % max_parts) for e in s_built[1:1 + n]]
+    assert n == int(s_call[0]) == len(oracle.decode_items(b.seq_lens, nd, window, S))
+    cost = {(r, p): c for r, p, c in oracle.decode_items(b.seq_lens, nd, window, S)}
+    listed = [(int(e) // max_segs, int(e) % max_segs) for e in s_built[1:1 + n]]
     assert sorted(listed) == sorted(cost)
-    assert [cost[x] for x in listed] == [cost[(int(e) // max_parts, int(e) % max_parts)]
+    assert [cost[x] for x in listed] == [cost[(int(e) // max_segs, int(e) % max_segs)]
                                          for e in s_call[1:1 + n]]       # same cost order
     # the prescheduled call reads the built schedule and writes what the plain call wrote;
     # a fresh workspace shows that it builds nothing there
