@@ -313,8 +313,8 @@ def fp8_decode_report(dev, seed):
     """Decode over an E4M3 cache (attn_fp8_decode_fwd) against the bf16 cache
     (attn_varlen_fwd) on the paged GQA decode workload (256 requests, contexts U[512, 8192],
     32 q / 8 kv heads, d 128, block 16) and on the mixed workload's 120 decode requests
-    (pass 0), with the library's default partition (partition_tokens 0) and 2048, 4096 and
-    8192 keys. Algorithmic bytes: each request's visible K and V once (2 bytes per element in
+    (pass 0), with the library's default partition (partition_tokens 0) and 512, 1024, 2048,
+    4096 and 8192 keys. Algorithmic bytes: each request's visible K and V once (2 bytes per element in
     bf16, 1 in E4M3) plus q, out, lse and the block-table entries. One JSON line per
     workload, cache type and partition length."""
     import torch
@@ -346,7 +346,7 @@ def fp8_decode_report(dev, seed):
                                  block_size=b.block_size,
                                  max_blocks_per_seq=b.max_blocks_per_seq, dtype=A.ATTN_BF16,
                                  partition_tokens=pt)
-                 for pt in (0, 2048, 4096, 8192)}
+                 for pt in (0, 512, 1024, 2048, 4096, 8192)}
         # one workspace large enough for the shortest partitions (the most partials)
         ws = torch.empty(max(A.attn_workspace_bytes(dd) for dd in descs.values()),
                          dtype=torch.uint8, device=dev)
@@ -633,9 +633,11 @@ def ceilings_report(dev):
 
 
 def mixed_step(batch, layers, dev):
-    """The timed step's launch configuration: per layer pass, the decode rows (split-KV kernel
-    + LSE merge, their own descriptor) and the prefill rows (prefill kernel, query starts
-    rebased to 0). Within a pass the two row sets are independent, so the decode call goes to
+    """The timed step's launch configuration: at the start of the step, the decode work
+    schedule of each distinct window (it depends only on the decode rows' seq_lens, so one
+    build serves every pass with that window); per layer pass, the decode rows (split-KV
+    kernel + LSE merge, their own descriptor, reading the prebuilt schedule) and the prefill
+    rows (prefill kernel, query starts rebased to 0). Within a pass the two row sets are independent, so the decode call goes to
     a second stream (default priority) forked from torch's current stream at the start of the
     pass and joined back at its end, while the prefill call runs on the current stream: the
     HBM-bound decode kernels then run beside the MFMA-bound prefill kernel on the CUs its
@@ -663,9 +665,13 @@ def mixed_step(batch, layers, dev):
     desc_pre = A.make_desc(num_seqs=batch.num_seqs - nd, num_tokens=batch.num_tokens - tok0,
                            num_decodes=0, max_query_len=int(batch.query_lens[nd:].max()),
                            max_seq_len=int(batch.seq_lens[nd:].max()), **common)
-    # one decode workspace per pass
+    # one decode workspace per pass; one decode work schedule per distinct window, built once
+    # per step (batch) at its start and read by every pass with that window
     wss = [torch.empty(A.attn_workspace_bytes(desc_dec), dtype=torch.uint8, device=dev)
            for _ in layers]
+    windows = sorted({w for _, w in batch.passes})
+    scheds = {w: torch.empty(max(A.attn_decode_schedule_bytes(desc_dec, w) // 4, 1),
+                             dtype=torch.int32, device=dev) for w in windows}
     outs = [torch.empty_like(q) for q, _ in layers]
     lses = [torch.empty(batch.num_tokens, batch.num_heads, dtype=torch.float32, device=dev)
             for _ in layers]
@@ -674,6 +680,10 @@ def mixed_step(batch, layers, dev):
     fork, join = torch.cuda.Event(), torch.cuda.Event()
 
     def step(ev=None):
+        fork.record(stream)
+        dec_stream.wait_event(fork)
+        for w in windows:
+            A.attn_build_decode_schedule(desc_dec, sl_dec, w, scheds[w], dec_stream)
         for li, (q, kv) in enumerate(layers):
             causal, window = batch.passes[li]
             # a layer pass starts when the previous one has ended on both streams (a model's
@@ -682,8 +692,10 @@ def mixed_step(batch, layers, dev):
             dec_stream.wait_event(fork)
             if ev is not None:
                 ev[li][0].record(dec_stream)
-            A.attn_varlen_fwd(desc_dec, q[:nd], kv, bt_dec, qsl_dec, sl_dec, batch.scale,
-                              causal, window, outs[li][:nd], lses[li][:nd], wss[li], dec_stream)
+            A.attn_varlen_fwd_prescheduled(desc_dec, q[:nd], kv, bt_dec, qsl_dec, sl_dec,
+                                           batch.scale, causal, window, outs[li][:nd],
+                                           lses[li][:nd], wss[li],
+                                           decode_schedule=scheds[window], stream=dec_stream)
             if ev is not None:
                 ev[li][1].record(dec_stream)
                 ev[li][2].record(stream)
@@ -836,8 +848,9 @@ def main():
                           "2.5 PFLOP/s; decode_frac = unique decode bytes / the decode calls' "
                           "spans / 8 TB/s; the spans overlap (two streams), so each is below "
                           "what its kernels reach alone; value combines both floors",
-        "launch": "per layer pass one decode-rows call and one prefill-rows call; the decode "
-                  "calls on a second stream beside the prefill calls (prefill and decode "
+        "launch": "per step the decode work schedule of each distinct window (2), then per "
+                  "layer pass one decode-rows call reading it and one prefill-rows call; the "
+                  "decode work on a second stream beside the prefill calls (prefill and decode "
                   "times above are each call's own event-timed span, overlapping)",
         "per_pass": per_pass,
         "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128, true, false> "
