@@ -718,6 +718,75 @@ def mixed_step(batch, layers, dev):
     return step, outs, lses
 
 
+def mixed_one_launch_step(batch, layers, dev):
+    """The mixed workload with one launch per layer pass (attn_varlen_fwd_mixed): at the start
+    of the step the prefill work schedule of each distinct (causal, window) is built (one
+    small kernel each, serving every pass with that mask); per pass one launch takes the
+    decode rows (one wave per request and kv head group, no split-KV partitions) and the
+    prefill rows. Returns step(ev=None) and the out / lse tensors (one per pass); with ev,
+    step records ev[pass][0..1] around the pass's launch."""
+    import torch
+    import exact_softmax_attention_paged_amd as A
+    bt, qsl, sl = (torch.from_numpy(x).to(dev) for x in (batch.block_table,
+                                                         batch.query_start_loc, batch.seq_lens))
+    desc = A.make_desc(num_seqs=batch.num_seqs, num_tokens=batch.num_tokens,
+                       num_decodes=batch.num_decodes, max_query_len=batch.max_query_len,
+                       max_seq_len=batch.max_seq_len, num_heads=batch.num_heads,
+                       num_kv_heads=batch.num_kv_heads, head_size=batch.head_size,
+                       num_blocks=batch.num_blocks, block_size=batch.block_size,
+                       max_blocks_per_seq=batch.max_blocks_per_seq, dtype=A.ATTN_BF16)
+    masks = sorted(set(batch.passes))
+    scheds = {m: torch.empty(A.attn_schedule_bytes(desc) // 4, dtype=torch.int32, device=dev)
+              for m in masks}
+    outs = [torch.empty_like(q) for q, _ in layers]
+    lses = [torch.empty(batch.num_tokens, batch.num_heads, dtype=torch.float32, device=dev)
+            for _ in layers]
+
+    def step(ev=None):
+        for m in masks:
+            A.attn_build_schedule(desc, qsl, sl, m[0], m[1], scheds[m])
+        for li, (q, kv) in enumerate(layers):
+            causal, window = batch.passes[li]
+            if ev is not None:
+                ev[li][0].record()
+            A.attn_varlen_fwd_mixed(desc, q, kv, bt, qsl, sl, batch.scale, causal, window,
+                                    outs[li], lses[li], scheds[(causal, window)])
+            if ev is not None:
+                ev[li][1].record()
+
+    return step, outs, lses
+
+
+def mixed_launch_report(dev, seed, steps=10, warmup=3):
+    """The mixed workload's step two ways: bench's timed configuration (per pass a decode
+    call on a second stream beside a prefill call) and one attn_varlen_fwd_mixed launch per
+    pass. One JSON line each: wall ms per step and the per-pass launch spans."""
+    import torch
+    import gen
+    batch = gen.config(5, seed=seed)
+    layers = [gen.make_tensors(batch, seed, dev, layer=li) for li in range(len(batch.passes))]
+    for name, make in (("two-stream", mixed_step), ("one-launch", mixed_one_launch_step)):
+        step, _, _ = make(batch, layers, dev)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in layers]
+               for _ in range(steps)]
+        t0 = time.perf_counter()
+        for s_ in range(steps):
+            step(evs[s_])
+        torch.cuda.synchronize()
+        ms = 1e3 * (time.perf_counter() - t0) / steps
+        rec = {"report": "mixed-launch", "step": name, "ms_per_step": round(ms, 4)}
+        if name == "one-launch":
+            rec["pass_ms"] = [round(float(np.mean([e[li][0].elapsed_time(e[li][1])
+                                                   for e in evs])), 4)
+                              for li in range(len(layers))]
+        print(json.dumps(rec), flush=True)
+        del step
+        torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -731,7 +800,7 @@ def main():
                     help="write profiles/prefill_traffic.json from two rocprofv3 --pmc runs")
     ap.add_argument("--record-command", default="", help="command line stored with the record")
     ap.add_argument("--report", choices=["configs", "cascade", "kv-write", "fp8-decode",
-                                         "schedule", "ceilings"],
+                                         "schedule", "ceilings", "mixed-launch"],
                     help="instead of the headline step, time one of the next-step paths "
                          "against the plain path and print one JSON line per batch")
     args = ap.parse_args()
@@ -771,6 +840,9 @@ def main():
         return
     if args.report == "ceilings":
         ceilings_report(dev)
+        return
+    if args.report == "mixed-launch":
+        mixed_launch_report(dev, args.seed)
         return
     batch = gen.config(5, seed=args.seed)
     layers = [gen.make_tensors(batch, args.seed, dev, layer=li) for li in range(len(batch.passes))]

@@ -27,6 +27,7 @@ EXPORTED = ("attn_workspace_bytes", "attn_decode_partition_tokens", "attn_varlen
             "attn_fp8_decode_fwd", "attn_schedule_bytes", "attn_build_schedule",
             "attn_varlen_fwd_scheduled", "attn_decode_schedule_bytes",
             "attn_build_decode_schedule", "attn_varlen_fwd_prescheduled",
+            "attn_varlen_fwd_mixed",
             "attn_varlen_fwd_noalloc", "attn_status_str")
 # bytes of the library's fixed device array used by attn_varlen_fwd_noalloc
 NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
@@ -102,6 +103,9 @@ def lib():
         L.attn_varlen_fwd_prescheduled.argtypes = [P(attn_desc), vp, vp, vp, vp, vp, f32, i32,
                                                    i32, vp, vp, vp, sz, vp, sz, vp, sz, vp]
         L.attn_varlen_fwd_prescheduled.restype = i32
+        L.attn_varlen_fwd_mixed.argtypes = [P(attn_desc), vp, vp, vp, vp, vp, f32, i32, i32,
+                                            vp, vp, vp, sz, vp]
+        L.attn_varlen_fwd_mixed.restype = i32
         L.attn_check_slot_mapping_host.argtypes = [P(attn_desc), vp]
         L.attn_check_slot_mapping_host.restype = i32
         L.attn_status_str.argtypes = [i32]
@@ -532,3 +536,24 @@ def attn_varlen_fwd_prescheduled(desc: attn_desc, q, kv_cache, block_table, quer
         ds_bytes, ctypes.c_void_p(stream.cuda_stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_varlen_fwd_prescheduled")
+
+
+def attn_varlen_fwd_mixed(desc: attn_desc, q, kv_cache, block_table, query_start_loc, seq_lens,
+                          scale: float, causal: bool, window: int, out, lse, prefill_schedule,
+                          stream=None) -> None:
+    """One launch for a mixed batch: the decode rows one wave per (request, kv head group)
+    over all their keys, the prefill rows from ``prefill_schedule`` (attn_build_schedule).
+    Needs no workspace."""
+    import torch
+    _check_call("attn_varlen_fwd_mixed", desc, q, kv_cache, block_table, query_start_loc,
+                seq_lens, out, lse, None)
+    _check_tensor("prefill_schedule", prefill_schedule, torch.int32, q.device, allow_none=True)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    ps_bytes = 0 if prefill_schedule is None else prefill_schedule.numel() * 4
+    st = lib().attn_varlen_fwd_mixed(
+        ctypes.byref(desc), _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(query_start_loc),
+        _ptr(seq_lens), float(scale), 1 if causal else 0, int(window), _ptr(out), _ptr(lse),
+        _ptr(prefill_schedule), ps_bytes, ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_varlen_fwd_mixed")

@@ -600,6 +600,39 @@ attn_status attn_varlen_fwd_prescheduled(
   return ATTN_OK;
 }
 
+attn_status attn_varlen_fwd_mixed(const attn_desc* desc, const void* q, const void* kv_cache,
+                                  const int32_t* block_table, const int32_t* query_start_loc,
+                                  const int32_t* seq_lens, float scale, int32_t causal,
+                                  int32_t window, void* out, float* lse,
+                                  const int32_t* prefill_schedule, size_t prefill_schedule_bytes,
+                                  void* stream) {
+  attn_status s = check_desc(desc);
+  if (s != ATTN_OK) return s;
+  const attn_desc& d = *desc;
+  if (d.dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (window > 0 && !causal) return ATTN_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  size_t need_sched = 0;
+  s = attn_schedule_bytes(desc, &need_sched);
+  if (s != ATTN_OK) return s;
+  const bool has_prefill = d.num_seqs > d.num_decodes;
+  if (has_prefill && (prefill_schedule == nullptr || prefill_schedule_bytes < need_sched))
+    return ATTN_ERR_WORKSPACE;
+  if (d.num_seqs == 0 || d.num_tokens == 0) return ATTN_OK;
+  if (q == nullptr || kv_cache == nullptr || block_table == nullptr ||
+      query_start_loc == nullptr || seq_lens == nullptr || out == nullptr)
+    return ATTN_ERR_NULL;
+  attn::PrefillParams pp = prefill_params(d, q, kv_cache, block_table, query_start_loc,
+                                          seq_lens, scale, causal, window, out, lse);
+  const attn::DecodeParams dp = decode_params(d, pp, 1, nullptr);   // no partials: no workspace
+  pp.seq_begin = d.num_decodes;
+  pp.num_seqs = has_prefill ? d.num_seqs - d.num_decodes : 0;
+  pp.schedule = prefill_schedule;
+  pp.max_qtiles = (int32_t)schedule_max_qtiles(&d);
+  return attn::launch_mixed_bf16(pp, dp, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 attn_status attn_check_metadata_host(const attn_desc* desc, const int32_t* block_table,
                                      const int32_t* query_start_loc, const int32_t* seq_lens) {
   const attn_status s = check_desc(desc);

@@ -162,5 +162,8 @@ hipError_t launch_prefix_slices_merge(const PrefixMergeParams& p, int head_size,
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeParams& p, hipStream_t stream);   // E4M3 cache
+// One launch for a mixed batch: decode requests [0, dp.num_decodes) one wave per (request, kv
+// head group) over all their keys, and the prefill rows of p (p.schedule required).
+hipError_t launch_mixed_bf16(const PrefillParams& p, const DecodeParams& dp, hipStream_t stream);
 
 }  // namespace attn

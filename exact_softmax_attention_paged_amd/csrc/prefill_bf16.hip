@@ -32,6 +32,7 @@
 //   A (32 x 16): element e of lane l is A[l % 32][8h + e]
 //   B (16 x 32): element e of lane l is B[8h + e][l % 32]
 //   C (32 x 32): element e of lane l is C[8(e / 4) + 4h + e % 4][l % 32]
+#include "decode_core.hpp"
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -110,8 +111,15 @@ __device__ __forceinline__ const lds_shortx4* lds_at(uint32_t byte_addr) {
   return (const lds_shortx4*)(uintptr_t)byte_addr;
 }
 
+// Bytes of the K/V tile buffers of one workgroup.
+template <int D>
+constexpr int kv_lds_bytes() { return kBufs * 2 * tile_keys<D>() * 2 * D; }
+
+// The work of one prefill workgroup: q tile and q head from the schedule slot bx / num_heads
+// (scheduled launches) or from the grid; sKV: the workgroup's kv_lds_bytes<D>() of LDS.
 template <int D, bool CAUSAL, bool WINDOW>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const PrefillParams p) {
+__device__ __forceinline__ void prefill_wg(const PrefillParams& p, const uint32_t bx,
+                                           unsigned char* __restrict__ sKV) {
   constexpr int kBC = tile_keys<D>();   // keys per KV tile
   constexpr int kKT = kBC / 32;         // 32-key MFMA tiles per KV tile
   constexpr int KC = D / 16;          // 16-deep k-chunks of the QK^T contraction
@@ -129,9 +137,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
   constexpr int TILEB = kBC * ROWB;   // bytes of one K (or V) tile
   static_assert(IPW * kDmaWaves == NI, "tile rows must split evenly over the waves");
 
-  // [buffer][K, V] tiles, row-major [key][d] with 16-byte chunks XOR-swizzled per row; the
-  // next tile lands in one buffer while the other is consumed
-  __shared__ __attribute__((aligned(1024))) unsigned char sKV[kBufs * 2 * TILEB];
+  // sKV: [buffer][K, V] tiles, row-major [key][d] with 16-byte chunks XOR-swizzled per row;
+  // the next tile lands in one buffer while the other is consumed
+  static_assert(kBufs * 2 * TILEB == kv_lds_bytes<D>(), "LDS size");
 
   const bool single = p.single_ql > 0;          // cascade prefix pass: one sequence
   const int group = p.num_heads / p.num_kv_heads;
@@ -153,14 +161,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
     // item slot blockIdx.x / num_heads of the schedule (sorted longest first), q head
     // blockIdx.x % num_heads; slots past the item count have nothing to do (the buffer
     // holds an entry for every slot, so the item load is in bounds)
-    const int slot = blockIdx.x / p.num_heads;
+    const int slot = bx / p.num_heads;
     const int count = p.schedule[0];
     const int e = p.schedule[1 + slot];
     asm volatile("" ::"s"(count), "s"(e));       // one wait for both loads
     if (slot >= count) return;
     r = p.seq_begin + e / p.max_qtiles;
     qt = e % p.max_qtiles;
-    hq_grid = blockIdx.x % p.num_heads;
+    hq_grid = bx % p.num_heads;
   } else {
     r = single ? 0 : p.seq_begin + blockIdx.z;
     qt = gridDim.x - 1 - blockIdx.x;           // longest (causal) tiles are dispatched first
@@ -567,6 +575,50 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
 }
 
 template <int D, bool CAUSAL, bool WINDOW>
+__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char sKV[kv_lds_bytes<D>()];
+  prefill_wg<D, CAUSAL, WINDOW>(p, blockIdx.x, sKV);
+}
+
+// One launch for one layer pass of a mixed batch: the first dec_wgs workgroups take the decode
+// rows, one wave per (decode request, kv head, head group) streaming the request's visible
+// keys and writing its output (dec::decode_request_wave: no partitions, no merge, no
+// workspace), so the HBM-bound decode waves start at once on dec_wgs CUs; the other
+// workgroups are the prefill kernel's scheduled slots (p.schedule, sorted longest first).
+// Both kinds share one LDS allocation (the larger of their needs).
+template <int D, bool CAUSAL, bool WINDOW>
+__global__ __launch_bounds__(kThreads, 2) void mixed_bf16_kernel(const PrefillParams p,
+                                                                 const DecodeParams dp,
+                                                                 const int32_t dec_wgs) {
+  using T = dec::WaveTiles<D>;
+  constexpr int kWaveLds = (T::V_TILE + T::K_TILE) * 2;     // bytes of one decode wave's tiles
+  constexpr int kLds = kv_lds_bytes<D>() > kWaves * kWaveLds ? kv_lds_bytes<D>()
+                                                               : kWaves * kWaveLds;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
+  if ((int)blockIdx.x < dec_wgs) {
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int heads_wg = dp.num_kv_heads * ((dp.num_heads / dp.num_kv_heads + 15) / 16);
+    const int unit = (int)blockIdx.x * kWaves + w;
+    if (unit >= dp.num_decodes * heads_wg) return;
+    __bf16* tiles = reinterpret_cast<__bf16*>(lds + w * kWaveLds);
+    dec::decode_request_wave<D>(dp, unit / heads_wg, unit % heads_wg, tiles, tiles + T::V_TILE);
+    return;
+  }
+  prefill_wg<D, CAUSAL, WINDOW>(p, blockIdx.x - (uint32_t)dec_wgs, lds);
+}
+
+template <int D, bool CAUSAL, bool WINDOW>
+hipError_t launch_mixed(const PrefillParams& p, const DecodeParams& dp, hipStream_t stream) {
+  const int heads_wg = dp.num_kv_heads * ((dp.num_heads / dp.num_kv_heads + 15) / 16);
+  const int64_t dec_wgs = ((int64_t)dp.num_decodes * heads_wg + kWaves - 1) / kWaves;
+  const int64_t pre_wgs = p.num_seqs > 0 ? (int64_t)p.num_seqs * p.max_qtiles * p.num_heads : 0;
+  if (dec_wgs + pre_wgs == 0) return hipSuccess;
+  hipLaunchKernelGGL((mixed_bf16_kernel<D, CAUSAL, WINDOW>), dim3((unsigned)(dec_wgs + pre_wgs)),
+                     dim3(kThreads), 0, stream, p, dp, (int32_t)dec_wgs);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool WINDOW>
 hipError_t launch(const PrefillParams& p, hipStream_t stream) {
   dim3 grid((p.max_query_len + kBR - 1) / kBR, p.num_heads, p.num_seqs);
   if (p.schedule != nullptr) {       // one workgroup per (schedule slot, q head)
@@ -587,7 +639,21 @@ hipError_t launch_mask(const PrefillParams& p, hipStream_t stream) {
   return launch<D, false, false>(p, stream);
 }
 
+template <int D>
+hipError_t launch_mixed_mask(const PrefillParams& p, const DecodeParams& dp,
+                             hipStream_t stream) {
+  if (p.window > 0) return launch_mixed<D, true, true>(p, dp, stream);
+  if (p.causal) return launch_mixed<D, true, false>(p, dp, stream);
+  return launch_mixed<D, false, false>(p, dp, stream);
+}
+
 }  // namespace
+
+hipError_t launch_mixed_bf16(const PrefillParams& p, const DecodeParams& dp,
+                             hipStream_t stream) {
+  return p.head_size == 64 ? launch_mixed_mask<64>(p, dp, stream)
+                           : launch_mixed_mask<128>(p, dp, stream);
+}
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   if (p.num_seqs <= 0 || p.max_query_len <= 0) return hipSuccess;

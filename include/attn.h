@@ -393,6 +393,28 @@ attn_status attn_varlen_fwd_prescheduled(
     const int32_t* prefill_schedule, size_t prefill_schedule_bytes,
     const int32_t* decode_schedule, size_t decode_schedule_bytes, void* stream);
 
+/*
+ * attn_varlen_fwd_mixed: attn_varlen_fwd (bf16 only) as ONE kernel launch for a batch that mixes
+ * decode and prefill rows ([FA] "FA3의 AOT 스케줄링" section: one kernel serving mixed
+ * prefill + decode batches; [LIN] Prefill/Decode split section: requests [0, num_decodes) are
+ * the decode rows). Its first workgroups take the decode rows, one wave per (decode request, kv
+ * head, group of up to 16 q heads) streaming all of the request's visible keys with an online
+ * softmax and writing the output directly (no split-KV partitions, so no merge and no
+ * workspace); the other workgroups are the prefill kernel's, taking their (request, q tile)
+ * items from prefill_schedule (attn_build_schedule for the same descriptor, metadata, causal and
+ * window). Same inputs, outputs and masks as attn_varlen_fwd; the decode rows' results equal
+ * attn_varlen_fwd's up to the order of the fp32 softmax sums (one partition per request).
+ * Errors: those of attn_varlen_fwd except the workspace ones; ATTN_ERR_UNSUPPORTED for a dtype
+ * other than ATTN_BF16; ATTN_ERR_WORKSPACE when prefill rows exist and prefill_schedule is NULL
+ * or below attn_schedule_bytes(desc).
+ */
+attn_status attn_varlen_fwd_mixed(const attn_desc* desc, const void* q, const void* kv_cache,
+                                  const int32_t* block_table, const int32_t* query_start_loc,
+                                  const int32_t* seq_lens, float scale, int32_t causal,
+                                  int32_t window, void* out, float* lse,
+                                  const int32_t* prefill_schedule, size_t prefill_schedule_bytes,
+                                  void* stream);
+
 /* attn_status_str: static, NUL-terminated name of a status code ("ATTN_OK", ...). */
 const char* attn_status_str(int32_t status);
 

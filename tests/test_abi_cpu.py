@@ -375,6 +375,29 @@ def test_decode_schedule_sizes_and_errors():
         None, 0, FAKE, 256, None) == A.ATTN_ERR_WORKSPACE           # decode partials need it
 
 
+def test_mixed_argument_errors():
+    """The one-launch mixed call: bf16 only, window needs causal, a prefill schedule of the
+    right size whenever prefill rows exist; no workspace."""
+    lib = A.lib()
+
+    def mixed(desc, sched, sched_bytes, causal=1, window=0, q=FAKE):
+        return lib.attn_varlen_fwd_mixed(ctypes.byref(desc), q, FAKE, FAKE, FAKE, FAKE, 0.1,
+                                         causal, window, FAKE, None, sched, sched_bytes, None)
+    d = _desc()                                   # 1 decode + 1 prefill request
+    need = A.attn_schedule_bytes(d)
+    assert mixed(_desc(dtype=A.ATTN_F32), FAKE, need) == A.ATTN_ERR_UNSUPPORTED
+    assert mixed(d, FAKE, need, causal=0, window=8) == A.ATTN_ERR_UNSUPPORTED
+    assert mixed(d, None, 0) == A.ATTN_ERR_WORKSPACE
+    assert mixed(d, FAKE, need - 1) == A.ATTN_ERR_WORKSPACE
+    assert mixed(d, FAKE, need, q=None) == A.ATTN_ERR_NULL
+    assert mixed(_desc(block_size=24), FAKE, need) == A.ATTN_ERR_BLOCK_SIZE
+    # decode rows only: no schedule needed
+    only_dec = _desc(num_seqs=2, num_tokens=2, num_decodes=2, max_query_len=1)
+    assert mixed(only_dec, None, 0, q=None) == A.ATTN_ERR_NULL
+    # an empty batch is a no-op (nothing is read)
+    assert mixed(_desc(num_tokens=0), FAKE, need, q=None) == A.ATTN_OK
+
+
 def test_default_partition_follows_the_batch_size():
     """partition_tokens 0: the longest of 16384 ... 256 keys that still gives at least 2048
     split workgroups (decodes x kv heads x head groups x partitions of max_seq_len), else 256

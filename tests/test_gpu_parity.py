@@ -197,6 +197,63 @@ def test_workload5_bench_launch_parity(layer):
                             lambda bb, r: _rows_tile_edges(bb, r, window), chunk=2))
 
 
+@pytest.mark.parametrize("layer", [0, 1])
+def test_workload5_one_launch_parity(layer):
+    """One attn_varlen_fwd_mixed launch per layer pass (bench.mixed_one_launch_step): all
+    120 decode rows and the tile-edge rows of every prefill request."""
+    import dataclasses
+    import bench
+    b = gen.config(5)
+    q, kv = gen.make_tensors(b, 5, DEV, layer=layer)
+    bl = dataclasses.replace(b, passes=[b.passes[layer]])
+    causal, window = bl.passes[0]
+    print(f"[case] cfg5 layer {layer} in one launch", flush=True)
+    step, outs, lses = bench.mixed_one_launch_step(bl, [(q, kv)], torch.device(DEV))
+    step()
+    torch.cuda.synchronize()
+    print(_compare_requests(b, q, kv, outs[0], lses[0], causal, window,
+                            list(range(b.num_decodes)), _rows_all, chunk=20))
+    print(_compare_requests(b, q, kv, outs[0], lses[0], causal, window,
+                            list(range(b.num_decodes, b.num_seqs)),
+                            lambda bb, r: _rows_tile_edges(bb, r, window), chunk=2))
+
+
+ONE_LAUNCH = ["decode-then-prefill-d128-gqa8", "decode-d64-gqa20", "decode-d128-g1-bs512",
+              "mixed-d128-gqa4-bs48"]
+
+
+@pytest.mark.parametrize("name", ONE_LAUNCH)
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 37)],
+                         ids=["noncausal", "causal", "w37"])
+def test_one_launch_small_batches(name, causal, window):
+    """attn_varlen_fwd_mixed on small mixed batches, every row against the oracle; its
+    prefill rows run the prefill kernel's code and equal the plain call's bit for bit."""
+    kw = dict(SMALL)[name]
+    seed = 300 + ONE_LAUNCH.index(name)
+    b = _batch(seed, **kw)
+    print(f"[case] one launch {name} causal={causal} window={window}", flush=True)
+    q, kv = gen.make_tensors(b, seed, DEV, poison=True)
+    desc = A.make_desc(num_seqs=b.num_seqs, num_tokens=b.num_tokens, num_decodes=b.num_decodes,
+                       max_query_len=b.max_query_len, max_seq_len=b.max_seq_len,
+                       num_heads=b.num_heads, num_kv_heads=b.num_kv_heads,
+                       head_size=b.head_size, num_blocks=b.num_blocks,
+                       block_size=b.block_size, max_blocks_per_seq=b.max_blocks_per_seq,
+                       dtype=A.ATTN_BF16)
+    bt, qsl, sl = device_meta(b, DEV)
+    sched = torch.empty(A.attn_schedule_bytes(desc) // 4, dtype=torch.int32, device=DEV)
+    A.attn_build_schedule(desc, qsl, sl, causal, window, sched)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((b.num_tokens, b.num_heads), float("nan"), dtype=torch.float32, device=DEV)
+    A.attn_varlen_fwd_mixed(desc, q, kv, bt, qsl, sl, b.scale, causal, window, out, lse, sched)
+    out_p, lse_p = run_library(b, q, kv, causal, window)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_on(b, q, kv, causal, window)
+    compare(out, lse, ref_out, ref_lse, label=f"one launch {name}")
+    tok0 = int(b.query_start_loc[b.num_decodes])
+    assert torch.equal(out[tok0:].view(torch.int16), out_p[tok0:].view(torch.int16))
+    assert torch.equal(lse[tok0:], lse_p[tok0:])
+
+
 @pytest.mark.parametrize("causal,window", [(True, 0), (True, 8192)], ids=["causal", "w8192"])
 def test_very_long_contexts(causal, window):
     """Contexts of 100K-131K keys, past the workloads' 32K: decode rows split into up to 64
