@@ -139,14 +139,20 @@ def host_cpu_model() -> str:
     return "unknown"
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
-PREFILL_SRC = os.path.join(ROOT, "exact_softmax_attention_paged_amd", "csrc", "prefill_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mixed_pass_traffic.json")
+# the dominant kernel (one launch of a mixed layer pass) is built from these sources
+KERNEL_SRCS = [os.path.join(ROOT, "exact_softmax_attention_paged_amd", "csrc", f)
+               for f in ("prefill_bf16.hip", "decode_core.hpp")]
+DOMINANT_KERNEL = "mixed_bf16_kernel<128, true, false>"
 COPY_BYTES = 1 << 30
 
 
-def prefill_source_hash() -> str:
+def kernel_source_hash() -> str:
     import hashlib
-    return hashlib.sha256(open(PREFILL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def pmc_probe(dev):
@@ -162,8 +168,8 @@ def pmc_probe(dev):
 
 
 def record_traffic(fetch_csv, write_csv, command):
-    """Turn two rocprofv3 counter_collection.csv files into profiles/prefill_traffic.json:
-    per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of the prefill kernel, scaled by the bytes
+    """Turn two rocprofv3 counter_collection.csv files into profiles/mixed_pass_traffic.json:
+    per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of the attention kernels, scaled by the bytes
     the same counters report for the plain 1 GiB copy."""
     import csv
     import re
@@ -177,24 +183,24 @@ def record_traffic(fetch_csv, write_csv, command):
             acc.setdefault(name, []).append(float(row["Counter_Value"]))
         return acc
 
-    out = {"source_sha256_16": prefill_source_hash(), "command": command}
+    out = {"source_sha256_16": kernel_source_hash(), "command": command}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         acc = per_kernel(path, counter)
         # the calibration copies are the runtime's device-to-device copy kernel
         copy = sorted(v for n, vals in acc.items() if "rocclr_copyBuffer" in n for v in vals)
         pre = {re.sub(r"\(attn::.*$", "", n.replace("void ", "").replace(
             "attn::(anonymous namespace)::", "")): vals for n, vals in acc.items()
-            if "prefill_bf16_kernel" in n}
+            if "attn::" in n}
         copy_kib = copy[len(copy) // 2]
         expected_kib = COPY_BYTES / 1024.0
         factor = expected_kib / copy_kib
         out[counter] = {"copy_kib_per_dispatch": copy_kib, "copy_expected_kib": expected_kib,
                         "scale": factor,
-                        "prefill_kib_per_dispatch": {k: sum(v) / len(v) for k, v in pre.items()}}
-    # per launch of the dominant kernel (the causal prefill of layer pass 0)
-    f_kib = out["FETCH_SIZE"]["prefill_kib_per_dispatch"]
-    w_kib = out["WRITE_SIZE"]["prefill_kib_per_dispatch"]
-    key = "prefill_bf16_kernel<128, true, false>"
+                        "kib_per_dispatch": {k: sum(v) / len(v) for k, v in pre.items()}}
+    # per launch of the dominant kernel (the one launch of layer pass 0, causal)
+    f_kib = out["FETCH_SIZE"]["kib_per_dispatch"]
+    w_kib = out["WRITE_SIZE"]["kib_per_dispatch"]
+    key = DOMINANT_KERNEL
     out["kernel"] = key
     out["traffic_bytes_per_launch"] = (f_kib[key] * out["FETCH_SIZE"]["scale"] +
                                        w_kib[key] * out["WRITE_SIZE"]["scale"]) * 1024.0
@@ -204,13 +210,13 @@ def record_traffic(fetch_csv, write_csv, command):
 
 
 def recorded_traffic():
-    """Bytes per prefill launch from profiles/prefill_traffic.json, or None when the record is
-    missing or was taken on a different prefill kernel source."""
+    """HBM bytes per launch of the dominant kernel from profiles/mixed_pass_traffic.json, or
+    None when the record is missing or was taken on a different kernel source."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256_16") != prefill_source_hash():
+    if rec.get("source_sha256_16") != kernel_source_hash():
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -713,7 +719,18 @@ def mixed_step(batch, layers, dev):
         A.attn_varlen_fwd(desc_pre, q[tok0:], kv, bt_pre, qsl_pre, sl_pre, batch.scale,
                           causal, window, outs[li][tok0:], lses[li][tok0:], None, stream)
 
+    def decode_call(li):
+        """Layer pass li's decode-rows call alone (its window's schedule built by the last
+        step), on the current stream."""
+        q, kv = layers[li]
+        causal, window = batch.passes[li]
+        A.attn_varlen_fwd_prescheduled(desc_dec, q[:nd], kv, bt_dec, qsl_dec, sl_dec,
+                                       batch.scale, causal, window, outs[li][:nd],
+                                       lses[li][:nd], wss[li], decode_schedule=scheds[window],
+                                       stream=stream)
+
     step.prefill_call = prefill_call
+    step.decode_call = decode_call
 
     return step, outs, lses
 
@@ -797,7 +814,7 @@ def main():
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run the 1 GiB copy calibration before the timed steps")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/prefill_traffic.json from two rocprofv3 --pmc runs")
+                    help="write profiles/mixed_pass_traffic.json from two rocprofv3 --pmc runs")
     ap.add_argument("--record-command", default="", help="command line stored with the record")
     ap.add_argument("--report", choices=["configs", "cascade", "kv-write", "fp8-decode",
                                          "schedule", "ceilings", "mixed-launch"],
@@ -846,11 +863,11 @@ def main():
         return
     batch = gen.config(5, seed=args.seed)
     layers = [gen.make_tensors(batch, args.seed, dev, layer=li) for li in range(len(batch.passes))]
-    step, outs, lses = mixed_step(batch, layers, dev)
+    step, outs, lses = mixed_one_launch_step(batch, layers, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in layers]
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in layers]
            for _ in range(args.steps)]
     t_start = time.perf_counter()
     for s in range(args.steps):
@@ -859,36 +876,47 @@ def main():
     wall = time.perf_counter() - t_start
     ms_step = 1e3 * wall / args.steps
 
-    dec_ms = np.mean([sum(e[li][0].elapsed_time(e[li][1]) for li in range(len(layers)))
-                      for e in evs])
-    pre_ms_per_launch = np.mean([e[li][2].elapsed_time(e[li][3]) for e in evs
-                                 for li in range(len(layers))])
-    pre_ms = pre_ms_per_launch * len(layers)
     flops = dbytes_u = dbytes_l = 0.0
     per_pass = []
-    for (causal, window) in batch.passes:
+    for li, (causal, window) in enumerate(batch.passes):
         f, bu, bl = algorithmic_work(batch, causal, window)
         per_pass.append({"causal": causal, "window": window, "prefill_gflop": f / 1e9,
-                         "decode_gb_unique": bu / 1e9, "decode_gb_logical": bl / 1e9})
+                         "decode_gb_unique": bu / 1e9, "decode_gb_logical": bl / 1e9,
+                         "launch_ms": round(float(np.mean([e[li][0].elapsed_time(e[li][1])
+                                                           for e in evs])), 4)})
         flops += f
         dbytes_u += bu
         dbytes_l += bl
     floor_s = flops / PEAK_BF16_FLOPS + dbytes_u / PEAK_HBM_BYTES
     value = 100.0 * floor_s / (ms_step / 1e3)
-    # dominant kernel: the causal prefill launch of layer pass 0
-    pre0_ms = np.mean([e[0][2].elapsed_time(e[0][3]) for e in evs])
+    # dominant kernel: the one launch of layer pass 0 (causal), which holds the pass's decode
+    # rows and its causal prefill rows
+    pass0_ms = per_pass[0]["launch_ms"]
     flops0 = per_pass[0]["prefill_gflop"] * 1e9
-    achieved = flops0 / (pre0_ms / 1e3) / 1e12
+    bytes0 = per_pass[0]["decode_gb_unique"] * 1e9
+    achieved = flops0 / (pass0_ms / 1e3) / 1e12
     traffic = recorded_traffic()
-    # the same launch alone (no decode call beside it), after the timed region: the kernel's
-    # own roofline fraction, which the overlapped timing above does not show
-    alone = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
-    for e in alone:
-        e[0].record()
-        step.prefill_call(0)
-        e[1].record()
+
+    # after the timed region, each row set alone with the two-call helpers: the prefill rows'
+    # launch and the decode rows' calls of each pass (their kernels' own roofline fractions,
+    # which the combined launch does not show), and the two-stream step for comparison
+    ts_step, _, _ = mixed_step(batch, layers, dev)
+    for _ in range(2):
+        ts_step()
     torch.cuda.synchronize()
-    alone_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in alone]))
+
+    def timed(fn, reps=5):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for e in ev:
+            e[0].record()
+            fn()
+            e[1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    pre_alone = [timed(lambda li=li: ts_step.prefill_call(li)) for li in range(len(layers))]
+    dec_alone = [timed(lambda li=li: ts_step.decode_call(li)) for li in range(len(layers))]
+    ts_ms = timed(ts_step, 5)
+    alone_ms = pre_alone[0]
     achieved_alone = flops0 / (alone_ms / 1e3) / 1e12
     # the shader clock under a full MFMA load (own probe, right after the timed region): the
     # 2.5 PFLOP/s spec assumes 2.4 GHz, and the chip runs MFMA-bound kernels below that
@@ -897,8 +925,8 @@ def main():
     except Exception as exc:          # the probes library is optional for the headline line
         print(f"mfma probe unavailable: {exc}", file=sys.stderr)
         probe_tflops, sclk_mhz = None, None
-    pre_frac = flops / (pre_ms / 1e3) / PEAK_BF16_FLOPS
-    dec_frac = dbytes_u / (dec_ms / 1e3) / PEAK_HBM_BYTES
+    pre_frac = flops / (sum(pre_alone) / 1e3) / PEAK_BF16_FLOPS
+    dec_frac = dbytes_u / (sum(dec_alone) / 1e3) / PEAK_HBM_BYTES
     rec = {
         "metric": METRIC, "value": round(value, 3), "unit": "% of roofline",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -910,29 +938,38 @@ def main():
                                "(causal; causal + window 4096)",
                    "global_batch": batch.num_seqs, "num_tokens": batch.num_tokens,
                    "seed": args.seed, "parallelism": "none (1 GPU)"},
-        "prefill_tflops": round(flops / (pre_ms / 1e3) / 1e12, 2),
-        "decode_gbps": round(dbytes_u / (dec_ms / 1e3) / 1e9, 1),
-        "decode_gbps_logical": round(dbytes_l / (dec_ms / 1e3) / 1e9, 1),
-        "prefill_ms_per_step": round(pre_ms, 4), "decode_ms_per_step": round(dec_ms, 4),
+        "launch": "per step the prefill work schedule of each distinct mask (2 small kernels), "
+                  "then per layer pass ONE attn_varlen_fwd_mixed launch holding the decode rows "
+                  "(one wave per request and kv head, no split-KV partitions) and the prefill "
+                  "rows",
+        "two_stream_ms_per_step": round(ts_ms, 4),
+        "two_stream_note": "the same step as two calls per pass (decode rows split-KV on a "
+                           "second stream beside the prefill call), timed after the timed "
+                           "region",
+        "per_pass": per_pass,
+        "prefill_ms_alone": [round(x, 4) for x in pre_alone],
+        "decode_ms_alone": [round(x, 4) for x in dec_alone],
+        "prefill_tflops_alone": round(flops / (sum(pre_alone) / 1e3) / 1e12, 2),
+        "decode_gbps_alone": round(dbytes_u / (sum(dec_alone) / 1e3) / 1e9, 1),
         "prefill_frac": round(pre_frac, 4), "prefill_frac_target": 0.50,
         "decode_frac": round(dec_frac, 4), "decode_frac_target": 0.70,
-        "fractions_note": "prefill_frac = both passes' prefill flops / their event-timed spans / "
-                          "2.5 PFLOP/s; decode_frac = unique decode bytes / the decode calls' "
-                          "spans / 8 TB/s; the spans overlap (two streams), so each is below "
-                          "what its kernels reach alone; value combines both floors",
-        "launch": "per step the decode work schedule of each distinct window (2), then per "
-                  "layer pass one decode-rows call reading it and one prefill-rows call; the "
-                  "decode work on a second stream beside the prefill calls (prefill and decode "
-                  "times above are each call's own event-timed span, overlapping)",
-        "per_pass": per_pass,
-        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128, true, false> "
-                                                  "(causal prefill, layer pass 0)",
-                     "launch_ms": round(pre0_ms, 4), "flop_per_launch": flops0,
+        "fractions_note": "each row set alone after the timed region: prefill_frac = both "
+                          "passes' prefill flops / their prefill-rows launches / 2.5 PFLOP/s; "
+                          "decode_frac = unique decode bytes / the decode-rows calls (split-KV "
+                          "kernel + merge, prebuilt schedule) / 8 TB/s; value is the combined "
+                          "floor over the timed one-launch step",
+        "roofline": {"bound": "mfma", "kernel": DOMINANT_KERNEL +
+                     " (one launch: layer pass 0, its decode rows and causal prefill rows)",
+                     "launch_ms": pass0_ms, "flop_per_launch": flops0,
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_FLOPS / 1e12,
                      "unit": "TFLOP/s", "frac": round(achieved / (PEAK_BF16_FLOPS / 1e12), 4),
-                     "traffic": None if traffic is None else round(traffic)},
-        "roofline_alone": {"kernel": "prefill_bf16_kernel<128, true, false> (causal prefill, "
-                                     "layer pass 0), 5 launches alone after the timed region",
+                     "traffic": None if traffic is None else round(traffic),
+                     "decode_bytes_per_launch": bytes0,
+                     "floor_frac": round((flops0 / PEAK_BF16_FLOPS + bytes0 / PEAK_HBM_BYTES) /
+                                         (pass0_ms / 1e3), 4)},
+        "roofline_alone": {"kernel": "prefill_bf16_kernel<128, true, false> (the causal "
+                                     "prefill rows of layer pass 0 alone, 5 launches after the "
+                                     "timed region)",
                            "launch_ms": round(alone_ms, 4), "achieved": round(achieved_alone, 2),
                            "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                            "frac": round(achieved_alone / (PEAK_BF16_FLOPS / 1e12), 4)},

@@ -32,6 +32,8 @@
 //   A (32 x 16): element e of lane l is A[l % 32][8h + e]
 //   B (16 x 32): element e of lane l is B[8h + e][l % 32]
 //   C (32 x 32): element e of lane l is C[8(e / 4) + 4h + e % 4][l % 32]
+#include <algorithm>
+
 #include "decode_core.hpp"
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -581,11 +583,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(const Prefill
 }
 
 // One launch for one layer pass of a mixed batch: the first dec_wgs workgroups take the decode
-// rows, one wave per (decode request, kv head, head group) streaming the request's visible
-// keys and writing its output (dec::decode_request_wave: no partitions, no merge, no
-// workspace), so the HBM-bound decode waves start at once on dec_wgs CUs; the other
+// rows, each wave a (decode request, kv head, head group) unit at a time streaming the
+// request's visible keys and writing its output (dec::decode_request_wave: no partitions, no
+// merge, no workspace), so the HBM-bound decode waves start at once on dec_wgs CUs; the other
 // workgroups are the prefill kernel's scheduled slots (p.schedule, sorted longest first).
 // Both kinds share one LDS allocation (the larger of their needs).
+constexpr int kMixedDecodeWgs = 64;
 template <int D, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kThreads, 2) void mixed_bf16_kernel(const PrefillParams p,
                                                                  const DecodeParams dp,
@@ -598,10 +601,11 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_bf16_kernel(const PrefillPa
   if ((int)blockIdx.x < dec_wgs) {
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int heads_wg = dp.num_kv_heads * ((dp.num_heads / dp.num_kv_heads + 15) / 16);
-    const int unit = (int)blockIdx.x * kWaves + w;
-    if (unit >= dp.num_decodes * heads_wg) return;
     __bf16* tiles = reinterpret_cast<__bf16*>(lds + w * kWaveLds);
-    dec::decode_request_wave<D>(dp, unit / heads_wg, unit % heads_wg, tiles, tiles + T::V_TILE);
+    for (int unit = (int)blockIdx.x * kWaves + w; unit < dp.num_decodes * heads_wg;
+         unit += dec_wgs * kWaves)
+      dec::decode_request_wave<D>(dp, unit / heads_wg, unit % heads_wg, tiles,
+                                  tiles + T::V_TILE);
     return;
   }
   prefill_wg<D, CAUSAL, WINDOW>(p, blockIdx.x - (uint32_t)dec_wgs, lds);
@@ -610,7 +614,11 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_bf16_kernel(const PrefillPa
 template <int D, bool CAUSAL, bool WINDOW>
 hipError_t launch_mixed(const PrefillParams& p, const DecodeParams& dp, hipStream_t stream) {
   const int heads_wg = dp.num_kv_heads * ((dp.num_heads / dp.num_kv_heads + 15) / 16);
-  const int64_t dec_wgs = ((int64_t)dp.num_decodes * heads_wg + kWaves - 1) / kWaves;
+  // decode workgroups: one wave per unit up to kMixedDecodeWgs workgroups (their waves then
+  // take several units each) - enough waves to keep HBM busy while the CUs they hold are
+  // taken from the prefill work
+  const int64_t dec_wgs = std::min<int64_t>(
+      ((int64_t)dp.num_decodes * heads_wg + kWaves - 1) / kWaves, kMixedDecodeWgs);
   const int64_t pre_wgs = p.num_seqs > 0 ? (int64_t)p.num_seqs * p.max_qtiles * p.num_heads : 0;
   if (dec_wgs + pre_wgs == 0) return hipSuccess;
   hipLaunchKernelGGL((mixed_bf16_kernel<D, CAUSAL, WINDOW>), dim3((unsigned)(dec_wgs + pre_wgs)),
