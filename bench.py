@@ -558,7 +558,7 @@ def probes():
                                "`python -m exact_softmax_attention_paged_amd.build`")
         L = ctypes.CDLL(path)
         vp, i32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64
-        L.attn_probe_read_stream.argtypes = [vp, u64, vp, i32, vp]
+        L.attn_probe_read_stream.argtypes = [vp, u64, vp, i32, i32, vp]
         L.attn_probe_read_stream.restype = i32
         L.attn_probe_mfma_loop.argtypes = [vp, vp, i32, i32, vp]
         L.attn_probe_mfma_loop.restype = i32
@@ -587,7 +587,8 @@ def mfma_probe(dev, workgroups=256, iters=20000, reps=3):
 def ceilings_report(dev):
     """What this device delivers outside the attention kernels, beside the spec peaks the
     roofline fractions use. Own probes (libattn_probes.so, the instruction forms the kernels
-    use): a 4 GiB HBM read stream of 16-byte loads at several grid sizes, and back-to-back
+    use): a 4 GiB HBM read stream of 16-byte loads (plain, and non-temporal as the decode
+    kernel's K/V loads) at several grid sizes, and back-to-back
     v_mfma_f32_32x32x16_bf16 (8 waves per workgroup, 4 independent accumulators per wave) with
     the shader clock under that load. Vendor paths beside them: a bf16 GEMM through torch.mm
     (8192 x 8192 x 8192, contiguous operands) and a 4 GiB device-to-device copy (read + write
@@ -596,13 +597,14 @@ def ceilings_report(dev):
     import torch
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     src = torch.ones(1 << 30, device=dev, dtype=torch.int32)           # 4 GiB
-    for wgs in (1024, 2048, 4096, 8192, 16384):
+    for nt, wgs in [(0, w) for w in (1024, 2048, 4096, 8192, 16384)] + \
+            [(1, w) for w in (1024, 4096, 16384)]:
         sink = torch.empty(wgs * 256, device=dev, dtype=torch.int32)
         ms = _time_ms(lambda: probes().attn_probe_read_stream(
-            src.data_ptr(), src.numel() * 4, sink.data_ptr(), wgs, stream), 10)
+            src.data_ptr(), src.numel() * 4, sink.data_ptr(), wgs, nt, stream), 10)
         byts = src.numel() * 4.0
         print(json.dumps({"report": "ceilings", "what": f"own HBM read stream, 4 GiB, 16-byte "
-                          f"loads, {wgs} workgroups x 256 threads",
+                          f"{'non-temporal ' if nt else ''}loads, {wgs} workgroups x 256 threads",
                           "ms": round(ms, 4), "gbps": round(byts / (ms / 1e3) / 1e9, 1),
                           "frac_of_spec": round(byts / (ms / 1e3) / PEAK_HBM_BYTES, 4)}),
               flush=True)

@@ -14,6 +14,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int kReadThreads = 256;
 constexpr int kReadUnroll = 4;
 
+template <bool NT>
 __global__ __launch_bounds__(kReadThreads) void read_stream_kernel(const u32x4* __restrict__ src,
                                                                    uint64_t n, uint32_t* sink) {
   uint32_t acc = 0;
@@ -23,7 +24,10 @@ __global__ __launch_bounds__(kReadThreads) void read_stream_kernel(const u32x4* 
     // n is a multiple of kReadThreads * kReadUnroll, so a chunk that starts below n is whole
     u32x4 v[kReadUnroll];
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) v[u] = src[base + (uint64_t)u * kReadThreads];
+    for (int u = 0; u < kReadUnroll; ++u) {
+      const u32x4* a = src + base + (uint64_t)u * kReadThreads;
+      v[u] = NT ? __builtin_nontemporal_load(a) : *a;
+    }
 #pragma unroll
     for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
@@ -83,14 +87,19 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_loop_kernel(uint64_t* cl
 extern "C" {
 
 int32_t attn_probe_read_stream(const void* src, uint64_t bytes, uint32_t* sink,
-                               int32_t workgroups, void* stream) {
+                               int32_t workgroups, int32_t nontemporal, void* stream) {
   if (src == nullptr || sink == nullptr || bytes == 0 ||
       bytes % (16 * kReadThreads * kReadUnroll) != 0 ||
       (uintptr_t)src % 16 != 0 || workgroups <= 0)
     return 1;
-  hipLaunchKernelGGL(read_stream_kernel, dim3(workgroups), dim3(kReadThreads), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
-                     bytes / 16, sink);
+  if (nontemporal)
+    hipLaunchKernelGGL(read_stream_kernel<true>, dim3(workgroups), dim3(kReadThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
+                       bytes / 16, sink);
+  else
+    hipLaunchKernelGGL(read_stream_kernel<false>, dim3(workgroups), dim3(kReadThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
+                       bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

@@ -28,12 +28,13 @@ extern "C" {
 /*
  * attn_probe_read_stream: read `bytes` bytes of device memory at `src` (16-byte aligned, bytes a
  * positive multiple of 16 KiB) once, with 16-byte loads, `workgroups` workgroups of 256 threads
- * walking the buffer grid-stride with 4 loads in flight per thread. The loaded words are folded
- * (xor) into one uint32 per thread written to sink[workgroups * 256], so no load can be
- * dropped. Bytes moved: `bytes` read, workgroups * 1 KiB written.
+ * walking the buffer grid-stride with 4 loads in flight per thread; nontemporal != 0 marks
+ * every load non-temporal (the streaming hint the decode kernel's K/V loads carry). The loaded
+ * words are folded (xor) into one uint32 per thread written to sink[workgroups * 256], so no
+ * load can be dropped. Bytes moved: `bytes` read, workgroups * 1 KiB written.
  */
 int32_t attn_probe_read_stream(const void* src, uint64_t bytes, uint32_t* sink,
-                               int32_t workgroups, void* stream);
+                               int32_t workgroups, int32_t nontemporal, void* stream);
 
 /*
  * attn_probe_mfma_loop: `workgroups` workgroups of 8 waves (two per SIMD, as the prefill
