@@ -160,9 +160,14 @@ __device__ __forceinline__ void prefill_wg(const PrefillParams& p, const uint32_
                "s"(p.num_seqs), "s"(gridDim.x));
   int r, qt, hq_grid;
   if (p.schedule != nullptr) {
-    // item slot blockIdx.x / num_heads of the schedule (sorted longest first), q head
-    // blockIdx.x % num_heads; slots past the item count have nothing to do (the buffer
-    // holds an entry for every slot, so the item load is in bounds)
+    // item slot bx / num_heads of the schedule (sorted longest first), q head from
+    // j = bx % num_heads; slots past the item count have nothing to do (the buffer holds an
+    // entry for every slot, so the item load is in bounds). Workgroup ids go to the 8 XCDs
+    // in turn and each XCD has its own L2, so when num_heads is a multiple of 8 the head is
+    // (j % 8) * (num_heads / 8) + j / 8: the XCD of a workgroup then depends on its head
+    // block only, and every q tile of a (request, kv head) - whose q heads share the K/V
+    // tiles - runs on one XCD and reads them through one L2. (With the head = j order each
+    // XCD read every kv head's K/V for every q tile: 6x the HBM/MALL fetches.)
     const int slot = bx / p.num_heads;
     const int count = p.schedule[0];
     const int e = p.schedule[1 + slot];
@@ -170,11 +175,23 @@ __device__ __forceinline__ void prefill_wg(const PrefillParams& p, const uint32_
     if (slot >= count) return;
     r = p.seq_begin + e / p.max_qtiles;
     qt = e % p.max_qtiles;
-    hq_grid = bx % p.num_heads;
+    const int j = bx % p.num_heads;
+    hq_grid = p.num_heads % 8 == 0 ? (j % 8) * (p.num_heads / 8) + j / 8 : j;
   } else {
-    r = single ? 0 : p.seq_begin + blockIdx.z;
-    qt = gridDim.x - 1 - blockIdx.x;           // longest (causal) tiles are dispatched first
-    hq_grid = blockIdx.y;
+    // the grid (q tiles, heads, requests); longest (causal) q tiles first. When num_heads is
+    // a multiple of 8 (not in the prefix pass) the grid is read in its linear order, heads
+    // fastest, with the heads placed on the XCDs as in the scheduled mode above. Written with
+    // selects rather than branches: with an if / else-if / else here the compiler left the
+    // head undefined on the non-remapped path (no copy of the workgroup id y on that edge of
+    // the merged control flow), so heads were garbage there.
+    const bool remap = !single && p.num_heads % 8 == 0;
+    const uint32_t id = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const uint32_t per_req = gridDim.x * (uint32_t)p.num_heads;
+    const int local = (int)(id % per_req);
+    const int j = local % p.num_heads;
+    r = remap ? p.seq_begin + (int)(id / per_req) : (single ? 0 : p.seq_begin + (int)blockIdx.z);
+    qt = (int)gridDim.x - 1 - (remap ? local / p.num_heads : (int)blockIdx.x);
+    hq_grid = remap ? (j % 8) * (p.num_heads / 8) + j / 8 : (int)blockIdx.y;
   }
   r = __builtin_amdgcn_readfirstlane(r);            // wave-uniform
   qt = __builtin_amdgcn_readfirstlane(qt);
