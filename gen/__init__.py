@@ -160,28 +160,28 @@ def config(k: int, seed: Optional[int] = None) -> Batch:
     s = k if seed is None else seed
     rng = _rng(s, _S_LENGTHS)
     if k == 1:
-        return make_batch("cfg1", num_heads=4, num_kv_heads=4, head_size=64, block_size=256,
-                          dtype="f32", query_lens=[256], seq_lens=[256], passes=[(True, 0)],
+        return make_batch("tiny-causal-f32", num_heads=4, num_kv_heads=4, head_size=64,
+                          block_size=256, dtype="f32", query_lens=[256], seq_lens=[256], passes=[(True, 0)],
                           seed=s, scale=1.0 / 8.0)
     if k == 2:
-        return make_batch("cfg2", num_heads=16, num_kv_heads=16, head_size=64, block_size=512,
-                          dtype="bf16", query_lens=[512] * 8, seq_lens=[512] * 8,
+        return make_batch("bert-large-encoder", num_heads=16, num_kv_heads=16, head_size=64,
+                          block_size=512, dtype="bf16", query_lens=[512] * 8, seq_lens=[512] * 8,
                           passes=[(False, 0)], seed=s)
     if k == 3:
         sl = rng.integers(128, 1024, size=16, endpoint=True)
-        return make_batch("cfg3", num_heads=12, num_kv_heads=12, head_size=64, block_size=16,
-                          dtype="bf16", query_lens=sl, seq_lens=sl, passes=[(True, 0)],
+        return make_batch("gpt2-varlen-causal", num_heads=12, num_kv_heads=12, head_size=64,
+                          block_size=16, dtype="bf16", query_lens=sl, seq_lens=sl, passes=[(True, 0)],
                           seed=s, pool_factor=2)
     if k == 4:
         sl = rng.integers(512, 8192, size=256, endpoint=True)
-        return make_batch("cfg4", num_heads=32, num_kv_heads=8, head_size=128, block_size=16,
-                          dtype="bf16", query_lens=[1] * 256, seq_lens=sl,
+        return make_batch("paged-gqa-decode", num_heads=32, num_kv_heads=8, head_size=128,
+                          block_size=16, dtype="bf16", query_lens=[1] * 256, seq_lens=sl,
                           passes=[(True, 0)], seed=s)
     if k == 5:
         sl_dec = rng.integers(4096, 32768, size=120, endpoint=True)
         sl_pre = rng.integers(4096, 32768, size=8, endpoint=True)
-        return make_batch("cfg5", num_heads=64, num_kv_heads=8, head_size=128, block_size=64,
-                          dtype="bf16", query_lens=[1] * 120 + [2048] * 8,
+        return make_batch("mixed-long-context", num_heads=64, num_kv_heads=8, head_size=128,
+                          block_size=64, dtype="bf16", query_lens=[1] * 120 + [2048] * 8,
                           seq_lens=np.concatenate([sl_dec, sl_pre]),
                           passes=[(True, 0), (True, 4096)], seed=s,
                           shared_prefix_blocks=2048 // 64)

@@ -100,7 +100,7 @@ def test_workload5_cascade_sampled_parity():
     causal, window = b.passes[0]
     assert window == 0
     prefix = b.shared_prefix_blocks * b.block_size
-    print(f"[case] cfg5 cascade prefix={prefix}", flush=True)
+    print(f"[case] mixed long-context cascade prefix={prefix}", flush=True)
     q, kv = gen.make_tensors(b, 5, DEV, layer=0)
     out, lse = run_cascade(b, q, kv, causal, prefix)
     torch.cuda.synchronize()
@@ -115,4 +115,4 @@ def test_workload5_cascade_sampled_parity():
         rows_full.extend(b.query_start_loc[r] + pick)
     ref_out, ref_lse = oracle_on(sub, qs, kvs, causal, 0, rows=rows_sub)
     idx = torch.as_tensor(rows_full, device=out.device)
-    print(compare(out[idx], lse[idx], ref_out[rows_sub], ref_lse[rows_sub], label="cfg5 cascade"))
+    print(compare(out[idx], lse[idx], ref_out[rows_sub], ref_lse[rows_sub], label="mixed long-context cascade"))

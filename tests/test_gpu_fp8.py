@@ -82,7 +82,7 @@ def test_fp8_decode_workload4_shape_sampled():
     """The paged GQA decode workload's shape (256 requests, contexts U[512, 8192], 32 q / 8 kv
     heads, d 128, block 16) over an E4M3 cache, checked on sampled requests."""
     b = gen.config(4)
-    print("[case] fp8 decode cfg4 shape", flush=True)
+    print("[case] fp8 decode, paged GQA decode shape", flush=True)
     codes = fp8_cache(b, 4)
     q = gen.make_q(b, 4, DEV)
     out, lse = run_fp8_decode(b, q, torch.from_numpy(codes).to(DEV), 0,
@@ -95,7 +95,7 @@ def test_fp8_decode_workload4_shape_sampled():
                                                sub.block_table, sub.query_start_loc,
                                                sub.seq_lens, b.scale, True, 0)
     rows = torch.as_tensor(req, device=DEV)           # decode rows: token index = request
-    print(compare(out[rows], lse[rows], ref_out, ref_lse, label="cfg4 fp8"))
+    print(compare(out[rows], lse[rows], ref_out, ref_lse, label="paged GQA decode fp8"))
 
 
 @pytest.mark.parametrize("d", [64, 128])

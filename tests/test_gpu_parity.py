@@ -2,9 +2,10 @@
 
 Small batches (several tiles, ragged tails, every mask kind, GQA ratios 1..20, block sizes
 16..512, decode and prefill rows, NaN in every slot no request may read) are compared in
-full. The five workloads are run at full size in the bench's launch configuration: cfg1-3
-and cfg4 are compared in full (every row, every head), cfg5 on all of its decode rows and on
-the rows of its 2048-token prefill requests where the kernels change behaviour (query-tile
+full. The five workloads are run at full size in the bench's launch configuration: the tiny
+fp32, BERT-large-shaped, GPT-2-shaped and paged GQA decode workloads are compared in full
+(every row, every head), the mixed long-context workload on all of its decode rows and on the
+rows of its 2048-token prefill requests where the kernels change behaviour (query-tile
 edges, causal-diagonal and window-edge rows, plus seeded random rows)."""
 import zlib
 
@@ -86,11 +87,11 @@ def test_f32_matches_oracle(d, causal, window):
 def test_workload_full_parity(k):
     b = gen.config(k)
     causal, window = b.passes[0]
-    print(f"[case] cfg{k} full", flush=True)
+    print(f"[case] workload {k} ({b.name}) full", flush=True)
     q, kv = gen.make_tensors(b, k, DEV, poison=True)
     out, lse = run_library(b, q, kv, causal, window)
     ref_out, ref_lse = oracle_on(b, q, kv, causal, window)
-    print(compare(out, lse, ref_out, ref_lse, label=f"cfg{k}"))
+    print(compare(out, lse, ref_out, ref_lse, label=b.name))
 
 
 def _rows_all(b, r):
@@ -149,7 +150,7 @@ def test_workload4_full_parity(partition_tokens):
     the oracle: at its stated 512-token partitions (split-KV plus the LSE merge) and at the
     library default (what the per-workload report times)."""
     b = gen.config(4)
-    print(f"[case] cfg4 full size, all requests, partition {partition_tokens}", flush=True)
+    print(f"[case] paged GQA decode full size, all requests, partition {partition_tokens}", flush=True)
     q, kv = gen.make_tensors(b, 4, DEV)
     out, lse = run_library(b, q, kv, True, 0, partition_tokens=partition_tokens)
     torch.cuda.synchronize()
@@ -164,7 +165,7 @@ def test_workload5_full_decode_parity(layer):
     tile-edge rows of every prefill request, every q head, compared with the oracle."""
     b = gen.config(5)
     causal, window = b.passes[layer]
-    print(f"[case] cfg5 layer {layer} full size, all decode rows", flush=True)
+    print(f"[case] mixed long-context layer {layer} full size, all decode rows", flush=True)
     q, kv = gen.make_tensors(b, 5, DEV, layer=layer)
     out, lse = run_library(b, q, kv, causal, window)
     torch.cuda.synchronize()
@@ -186,7 +187,7 @@ def test_workload5_bench_launch_parity(layer):
     q, kv = gen.make_tensors(b, 5, DEV, layer=layer)
     bl = dataclasses.replace(b, passes=[b.passes[layer]])
     causal, window = bl.passes[0]
-    print(f"[case] cfg5 layer {layer} in the bench launch configuration", flush=True)
+    print(f"[case] mixed long-context layer {layer} in the bench launch configuration", flush=True)
     step, outs, lses = bench.mixed_step(bl, [(q, kv)], torch.device(DEV))
     step()
     torch.cuda.synchronize()
@@ -207,7 +208,7 @@ def test_workload5_one_launch_parity(layer):
     q, kv = gen.make_tensors(b, 5, DEV, layer=layer)
     bl = dataclasses.replace(b, passes=[b.passes[layer]])
     causal, window = bl.passes[0]
-    print(f"[case] cfg5 layer {layer} in one launch", flush=True)
+    print(f"[case] mixed long-context layer {layer} in one launch", flush=True)
     step, outs, lses = bench.mixed_one_launch_step(bl, [(q, kv)], torch.device(DEV))
     step()
     torch.cuda.synchronize()
