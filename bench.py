@@ -319,8 +319,8 @@ def fp8_decode_report(dev, seed):
     """Decode over an E4M3 cache (attn_fp8_decode_fwd) against the bf16 cache
     (attn_varlen_fwd) on the paged GQA decode workload (256 requests, contexts U[512, 8192],
     32 q / 8 kv heads, d 128, block 16) and on the mixed workload's 120 decode requests
-    (pass 0), with the library's default partition (partition_tokens 0) and 512, 1024, 2048,
-    4096 and 8192 keys. Algorithmic bytes: each request's visible K and V once (2 bytes per element in
+    (pass 0), with the library's default partition (partition_tokens 0: the batch-adapted
+    length for bf16, capped at 1024 keys for E4M3) and 512, 1024, 2048, 4096 and 8192 keys. Algorithmic bytes: each request's visible K and V once (2 bytes per element in
     bf16, 1 in E4M3) plus q, out, lse and the block-table entries. One JSON line per
     workload, cache type and partition length."""
     import torch
@@ -354,19 +354,25 @@ def fp8_decode_report(dev, seed):
                                  partition_tokens=pt)
                  for pt in (0, 512, 1024, 2048, 4096, 8192)}
         # one workspace large enough for the shortest partitions (the most partials)
-        ws = torch.empty(max(A.attn_workspace_bytes(dd) for dd in descs.values()),
+        ws = torch.empty(max(max(A.attn_workspace_bytes(dd),
+                                 A.attn_fp8_decode_workspace_bytes(dd)) for dd in descs.values()),
                          dtype=torch.uint8, device=dev)
         for pt, d_pt in descs.items():
-            runs.append(("bf16", pt, 2, lambda d_pt=d_pt: A.attn_varlen_fwd(
+            used = A.attn_decode_partition_tokens(d_pt)
+            runs.append(("bf16", pt, used, 2, lambda d_pt=d_pt: A.attn_varlen_fwd(
                 d_pt, q, kv, bt, qsl, sl, b.scale, True, 0, out, lse, ws)))
-            runs.append(("e4m3", pt, 1, lambda d_pt=d_pt: A.attn_fp8_decode_fwd(
-                d_pt, q, codes, bt, qsl, sl, b.scale, 0.0125, 0.02, 0, out, lse, ws)))
-        for name, pt, elem, fn in runs:
+            # the E4M3 default caps the partition at 1024 keys
+            runs.append(("e4m3", pt, min(used, 1024) if pt == 0 else used,
+                         1, lambda d_pt=d_pt: A.attn_fp8_decode_fwd(
+                             d_pt, q, codes, bt, qsl, sl, b.scale, 0.0125, 0.02, 0, out, lse,
+                             ws)))
+        for name, pt, used, elem, fn in runs:
             ms = _time_ms(fn, 20)
             byts = keys * 2 * b.num_kv_heads * b.head_size * elem + extra
             print(json.dumps({"report": "fp8-decode", "workload": gen.CONFIG_NAMES[k] +
                               (" (its 120 decode requests)" if k == 5 else ""), "cache": name,
-                              "partition_tokens": pt, "ms": round(ms, 4), "bytes": byts,
+                              "partition_tokens": pt, "partition_tokens_used": used,
+                              "ms": round(ms, 4), "bytes": byts,
                               "gbps": round(byts / (ms / 1e3) / 1e9, 1),
                               "frac_of_8tbps": round(byts / (ms / 1e3) / PEAK_HBM_BYTES, 4),
                               "tokens_per_s": round(keys / (ms / 1e3), 1)}), flush=True)
@@ -436,7 +442,9 @@ def configs_report(dev, seed):
     varlen prefill, the paged GQA decode, the mixed long-context batch) through one plain
     attn_varlen_fwd call per layer pass, with the library's default decode partition, and the
     paged GQA decode again at its stated 512-token partitions (each decode-only line also
-    times attn_varlen_fwd_prescheduled with the decode schedule built ahead, and the build). One JSON line per (workload,
+    times attn_varlen_fwd_prescheduled with the decode schedule built ahead, and the build;
+    each bf16 prefill-only line attn_varlen_fwd_scheduled with the prefill schedule built
+    ahead, and the build). One JSON line per (workload,
     pass, partition): mean call time by HIP events with the inputs hot in the caches, the
     algorithmic prefill TFLOP/s and decode GB/s of that call, and its % of the MI355X roofline,
     (prefill flops / MFMA peak + decode bytes / 8 TB/s) / call time, the MFMA peak being fp32
@@ -492,6 +500,19 @@ def configs_report(dev, seed):
                     pre = {"call_ms": round(tp, 4), "schedule_build_ms": round(tb, 4)}
                     pre.update(_rates(tp, 0, dec_unique, peak))
                     rec["prescheduled"] = pre
+                if b.num_decodes == 0 and not fp32:
+                    # the prefill work schedule built once ahead (once per batch and mask for
+                    # all its layers) and the call that dispatches its grid from it
+                    ps = torch.empty(A.attn_schedule_bytes(desc) // 4, dtype=torch.int32,
+                                     device=dev)
+                    tb = _time_ms(lambda: A.attn_build_schedule(desc, qsl, sl, causal, window,
+                                                                ps), reps)
+                    ts = _time_ms(lambda: A.attn_varlen_fwd_scheduled(
+                        desc, q, kv, bt, qsl, sl, b.scale, causal, window, out, lse, ws, ps),
+                        reps)
+                    sch = {"call_ms": round(ts, 4), "schedule_build_ms": round(tb, 4)}
+                    sch.update(_rates(ts, flops, 0, peak))
+                    rec["scheduled"] = sch
                 if k <= 3:
                     rec["cold"] = _cold_rates(A, b, desc, k, li, causal, window, bt, qsl, sl,
                                               ws, flops, peak, dev)
@@ -777,9 +798,10 @@ def mixed_one_launch_step(batch, layers, dev):
 
 
 def mixed_launch_report(dev, seed, steps=10, warmup=3):
-    """The mixed workload's step two ways: bench's timed configuration (per pass a decode
-    call on a second stream beside a prefill call) and one attn_varlen_fwd_mixed launch per
-    pass. One JSON line each: wall ms per step and the per-pass launch spans."""
+    """The mixed workload's step two ways: per pass a decode call on a second stream beside
+    a prefill call, and bench's timed configuration, one attn_varlen_fwd_mixed launch per
+    pass. One JSON line each: wall ms per step and, for the one-launch step, the per-pass
+    launch spans."""
     import torch
     import gen
     batch = gen.config(5, seed=seed)

@@ -24,7 +24,8 @@ ATTN_BF16, ATTN_F32 = 0, 1
 EXPORTED = ("attn_workspace_bytes", "attn_decode_partition_tokens", "attn_varlen_fwd", "attn_check_metadata_host",
             "attn_cascade_workspace_bytes", "attn_cascade_fwd", "attn_check_cascade_host",
             "attn_kv_cache_write", "attn_check_slot_mapping_host", "attn_kv_cache_write_fp8",
-            "attn_fp8_decode_fwd", "attn_schedule_bytes", "attn_build_schedule",
+            "attn_fp8_decode_workspace_bytes", "attn_fp8_decode_fwd", "attn_schedule_bytes",
+            "attn_build_schedule",
             "attn_varlen_fwd_scheduled", "attn_decode_schedule_bytes",
             "attn_build_decode_schedule", "attn_varlen_fwd_prescheduled",
             "attn_varlen_fwd_mixed",
@@ -86,6 +87,8 @@ def lib():
         L.attn_kv_cache_write_fp8.argtypes = [P(attn_desc), vp, i64, vp, i64, vp, f32, f32, vp,
                                               vp]
         L.attn_kv_cache_write_fp8.restype = i32
+        L.attn_fp8_decode_workspace_bytes.argtypes = [P(attn_desc), P(sz)]
+        L.attn_fp8_decode_workspace_bytes.restype = i32
         L.attn_fp8_decode_fwd.argtypes = [P(attn_desc), vp, vp, vp, vp, vp, f32, f32, f32, i32,
                                           vp, vp, vp, sz, vp]
         L.attn_fp8_decode_fwd.restype = i32
@@ -369,6 +372,15 @@ def attn_kv_cache_write_fp8(desc: attn_desc, key, value, slot_mapping, k_scale: 
                                        ctypes.c_void_p(stream.cuda_stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_kv_cache_write_fp8")
+
+
+def attn_fp8_decode_workspace_bytes(desc: attn_desc) -> int:
+    """Workspace bytes of attn_fp8_decode_fwd for desc (its E4M3 default partition)."""
+    n = ctypes.c_size_t(0)
+    st = lib().attn_fp8_decode_workspace_bytes(ctypes.byref(desc), ctypes.byref(n))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fp8_decode_workspace_bytes")
+    return int(n.value)
 
 
 def attn_fp8_decode_fwd(desc: attn_desc, q, kv_cache, block_table, query_start_loc, seq_lens,

@@ -299,10 +299,21 @@ attn_status attn_kv_cache_write_fp8(const attn_desc* desc, const void* key,
  * num_seqs, query_len 1 each) over an E4M3 cache: the same exact attention with K and V
  * dequantised (value(code) * k_scale, value(code) * v_scale). q and out are bf16 (desc->dtype
  * ATTN_BF16), lse fp32; the codes are converted to bf16 exactly (every E4M3 value is a bf16
- * value) and k_scale / v_scale are applied to the scores and the output in fp32. Workspace:
- * attn_workspace_bytes(desc). Errors: those of attn_varlen_fwd; ATTN_ERR_UNSUPPORTED for
- * num_decodes != num_seqs, a dtype other than ATTN_BF16, or scales that are not finite and > 0.
+ * value) and k_scale / v_scale are applied to the scores and the output in fp32. With
+ * desc->partition_tokens 0 the split-KV partition is attn_decode_partition_tokens' length
+ * capped at 1024 keys (E4M3 streams faster in the one-wave units of partitions up to 1024
+ * keys); a non-zero partition_tokens is used as given. Workspace:
+ * attn_fp8_decode_workspace_bytes(desc), which is at least attn_workspace_bytes(desc).
+ * Errors: those of attn_varlen_fwd; ATTN_ERR_UNSUPPORTED for num_decodes != num_seqs, a
+ * dtype other than ATTN_BF16, or scales that are not finite and > 0.
  */
+/*
+ * attn_fp8_decode_workspace_bytes: device workspace bytes that attn_fp8_decode_fwd needs for
+ * this descriptor (its partition as stated there), written to *bytes. Errors: ATTN_ERR_NULL
+ * (bytes null) and the descriptor errors of attn_workspace_bytes.
+ */
+attn_status attn_fp8_decode_workspace_bytes(const attn_desc* desc, size_t* bytes);
+
 attn_status attn_fp8_decode_fwd(const attn_desc* desc, const void* q, const void* kv_cache,
                                 const int32_t* block_table, const int32_t* query_start_loc,
                                 const int32_t* seq_lens, float scale, float k_scale,

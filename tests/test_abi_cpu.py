@@ -122,6 +122,31 @@ def test_workspace_size_and_check():
     assert big is not None
 
 
+def test_fp8_decode_workspace_uses_its_own_default_partition():
+    """The E4M3 decode's default partition is the bf16 default capped at 1024 keys; its
+    workspace query sizes for that, and for a stated partition equals attn_workspace_bytes."""
+    kw = dict(num_seqs=256, num_tokens=256, num_decodes=256, max_query_len=1, max_seq_len=8192,
+              num_heads=32, num_kv_heads=8, num_blocks=40000, max_blocks_per_seq=512)
+    d = _desc(**kw)
+    assert A.attn_decode_partition_tokens(d) == 16384     # bf16: one partition per request
+
+    def expected(decodes, heads, parts, segs):   # partition results, then the work schedule
+        return (-(-(decodes * heads * parts * (128 * 2 + 4)) // 256) * 256 +
+                -(-((1 + decodes * segs) * 4) // 256) * 256)
+    assert A.attn_workspace_bytes(d) == expected(256, 32, 1, 1)
+    # 1024-key partitions, one per 1024-key segment
+    assert A.attn_fp8_decode_workspace_bytes(d) == expected(256, 32, 8, 8)
+    for pt in (512, 4096):
+        dp = _desc(partition_tokens=pt, **kw)
+        assert A.attn_fp8_decode_workspace_bytes(dp) == A.attn_workspace_bytes(dp)
+    small = _desc()                                 # a default below 1024 keys is kept
+    assert A.attn_fp8_decode_workspace_bytes(small) >= A.attn_workspace_bytes(small)
+    n = ctypes.c_size_t(0)
+    assert A.lib().attn_fp8_decode_workspace_bytes(ctypes.byref(d), None) == A.ATTN_ERR_NULL
+    assert A.lib().attn_fp8_decode_workspace_bytes(ctypes.byref(_desc(block_size=24)),
+                                                   ctypes.byref(n)) == A.ATTN_ERR_BLOCK_SIZE
+
+
 def test_empty_batch_is_a_no_op():
     d = _desc(num_seqs=0, num_tokens=0, num_decodes=0, max_query_len=0, max_seq_len=0)
     assert _fwd(d, q=None, out=None) == A.ATTN_OK

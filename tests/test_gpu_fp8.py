@@ -44,7 +44,7 @@ def run_fp8_decode(b, q, codes_dev, window, ks=K_SCALE, vs=V_SCALE, partition_to
     desc.partition_tokens = partition_tokens
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=DEV)
-    n = A.attn_workspace_bytes(desc)
+    n = A.attn_fp8_decode_workspace_bytes(desc)
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
     A.attn_fp8_decode_fwd(desc, q, codes_dev, bt, qsl, sl, b.scale, ks, vs, window, out, lse, ws)
     return out, lse
@@ -78,15 +78,16 @@ def test_fp8_decode_matches_oracle(name, kw, window, pt):
     print(compare(out, lse, ref_out, ref_lse, label=name))
 
 
-def test_fp8_decode_workload4_shape_sampled():
+@pytest.mark.parametrize("pt", [512, 0], ids=["pt512", "default"])
+def test_fp8_decode_workload4_shape_sampled(pt):
     """The paged GQA decode workload's shape (256 requests, contexts U[512, 8192], 32 q / 8 kv
-    heads, d 128, block 16) over an E4M3 cache, checked on sampled requests."""
+    heads, d 128, block 16) over an E4M3 cache, checked on sampled requests, at the workload's
+    512-key partitions and at the E4M3 default (1024 keys here)."""
     b = gen.config(4)
-    print("[case] fp8 decode, paged GQA decode shape", flush=True)
+    print(f"[case] fp8 decode, paged GQA decode shape, partition {pt}", flush=True)
     codes = fp8_cache(b, 4)
     q = gen.make_q(b, 4, DEV)
-    out, lse = run_fp8_decode(b, q, torch.from_numpy(codes).to(DEV), 0,
-                              partition_tokens=512)       # the workload's partition length
+    out, lse = run_fp8_decode(b, q, torch.from_numpy(codes).to(DEV), 0, partition_tokens=pt)
     torch.cuda.synchronize()
     order = np.argsort(b.seq_lens)
     req = sorted(set(order[:6].tolist() + order[-6:].tolist() + [3, 100, 200]))

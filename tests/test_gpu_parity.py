@@ -220,7 +220,7 @@ def test_workload5_one_launch_parity(layer):
 
 
 ONE_LAUNCH = ["decode-then-prefill-d128-gqa8", "decode-d64-gqa20", "decode-d128-g1-bs512",
-              "mixed-d128-gqa4-bs48"]
+              "mixed-d128-gqa4-bs48", "mixed-d64-gqa4-bs80"]
 
 
 @pytest.mark.parametrize("name", ONE_LAUNCH)
