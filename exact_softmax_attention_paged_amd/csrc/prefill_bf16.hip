@@ -619,6 +619,18 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_bf16_kernel(const PrefillPa
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int heads_wg = dp.num_kv_heads * ((dp.num_heads / dp.num_kv_heads + 15) / 16);
     __bf16* tiles = reinterpret_cast<__bf16*>(lds + w * kWaveLds);
+    if (heads_wg % 8 == 0 && dec_wgs % 8 == 0) {
+      // Workgroup b runs on XCD b % 8 (each XCD has its own L2): its waves take only the
+      // (kv head, head group) units hw with hw % 8 == b % 8, every request in turn, so each
+      // XCD streams one eighth of the heads (the prefill workgroups of those kv heads' q heads
+      // run on the same XCD) and the shared prefix of a head is read by the waves of one L2.
+      const int x = (int)blockIdx.x % 8;
+      const int hpx = heads_wg / 8;                  // units per request on this XCD
+      const int n = dp.num_decodes * hpx;
+      for (int i = ((int)blockIdx.x / 8) * kWaves + w; i < n; i += (dec_wgs / 8) * kWaves)
+        dec::decode_request_wave<D>(dp, i / hpx, x + 8 * (i % hpx), tiles, tiles + T::V_TILE);
+      return;
+    }
     for (int unit = (int)blockIdx.x * kWaves + w; unit < dp.num_decodes * heads_wg;
          unit += dec_wgs * kWaves)
       dec::decode_request_wave<D>(dp, unit / heads_wg, unit % heads_wg, tiles,

@@ -41,6 +41,10 @@ SMALL = [
                                   d=128, bs=48)),
     ("mixed-d64-gqa4-bs80", dict(ql=[1, 150, 3], sl=[3000, 1500, 81], hq=4, hkv=1, d=64,
                                  bs=80)),
+    # 8 decodes x 8 kv heads: the one-launch kernel's 8 decode workgroups each take one kv head
+    ("decode8-kv8-then-prefill", dict(ql=[1] * 8 + [70], sl=[900, 33, 2500, 64, 1, 700, 1300,
+                                                           129, 300], hq=16, hkv=8, d=128,
+                                      bs=16)),
 ]
 MASKS = [(False, 0), (True, 0), (True, 1), (True, 100), (True, 513)]
 
@@ -220,7 +224,7 @@ def test_workload5_one_launch_parity(layer):
 
 
 ONE_LAUNCH = ["decode-then-prefill-d128-gqa8", "decode-d64-gqa20", "decode-d128-g1-bs512",
-              "mixed-d128-gqa4-bs48", "mixed-d64-gqa4-bs80"]
+              "mixed-d128-gqa4-bs48", "mixed-d64-gqa4-bs80", "decode8-kv8-then-prefill"]
 
 
 @pytest.mark.parametrize("name", ONE_LAUNCH)
