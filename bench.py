@@ -801,7 +801,8 @@ def mixed_launch_report(dev, seed, steps=10, warmup=3):
     """The mixed workload's step two ways: per pass a decode call on a second stream beside
     a prefill call, and bench's timed configuration, one attn_varlen_fwd_mixed launch per
     pass. One JSON line each: wall ms per step and, for the one-launch step, the per-pass
-    launch spans."""
+    launch spans. Then, per pass, the decode rows alone through the one-launch kernel (its 64
+    decode workgroups) and through the split-KV call."""
     import torch
     import gen
     batch = gen.config(5, seed=seed)
@@ -826,6 +827,33 @@ def mixed_launch_report(dev, seed, steps=10, warmup=3):
         print(json.dumps(rec), flush=True)
         del step
         torch.cuda.synchronize()
+    # the decode rows alone, through the one-launch kernel (its decode workgroups only) and
+    # through the split-KV call: what one CU streams when the decode side runs by itself
+    import exact_softmax_attention_paged_amd as A
+    b = gen.subset_meta(batch, list(range(batch.num_decodes)))
+    q = layers[0][0][:b.num_tokens].contiguous()
+    kv = layers[0][1]
+    bt, qsl, sl = (torch.from_numpy(x).to(dev) for x in (b.block_table, b.query_start_loc,
+                                                         b.seq_lens))
+    desc = A.make_desc(num_seqs=b.num_seqs, num_tokens=b.num_tokens, num_decodes=b.num_decodes,
+                       max_query_len=1, max_seq_len=b.max_seq_len, num_heads=b.num_heads,
+                       num_kv_heads=b.num_kv_heads, head_size=b.head_size,
+                       num_blocks=b.num_blocks, block_size=b.block_size,
+                       max_blocks_per_seq=b.max_blocks_per_seq, dtype=A.ATTN_BF16)
+    out = torch.empty_like(q)
+    lse = torch.empty(b.num_tokens, b.num_heads, dtype=torch.float32, device=dev)
+    ws = torch.empty(A.attn_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    for li, (causal, window) in enumerate(batch.passes):
+        _, dbytes, _ = algorithmic_work(batch, causal, window)
+        tm = _time_ms(lambda: A.attn_varlen_fwd_mixed(desc, q, kv, bt, qsl, sl, b.scale, causal,
+                                                      window, out, lse, None), 10)
+        tp = _time_ms(lambda: A.attn_varlen_fwd(desc, q, kv, bt, qsl, sl, b.scale, causal,
+                                                window, out, lse, ws), 10)
+        print(json.dumps({"report": "mixed-launch", "step": f"decode rows alone, pass {li}",
+                          "one_launch_kernel_ms": round(tm, 4), "split_kv_call_ms": round(tp, 4),
+                          "decode_gb_unique": round(dbytes / 1e9, 3),
+                          "one_launch_kernel_tbps": round(dbytes / tm / 1e9, 2),
+                          "split_kv_call_tbps": round(dbytes / tp / 1e9, 2)}), flush=True)
 
 
 def main():
