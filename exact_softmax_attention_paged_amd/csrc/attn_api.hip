@@ -75,6 +75,7 @@ attn_status check_desc(const attn_desc* d) {
       (d->partition_tokens > 0 && d->partition_tokens % 128 != 0))
     return ATTN_ERR_UNSUPPORTED;
   if (d->num_seqs > 65535) return ATTN_ERR_SHAPE;                    // grid z limit
+  if (ceil_div(d->max_query_len, 256) > 65535) return ATTN_ERR_SHAPE;  // q tiles: grid z limit
   if ((int64_t)d->max_seq_len > (int64_t)d->max_blocks_per_seq * d->block_size)
     return ATTN_ERR_SHAPE;
   if ((int64_t)d->max_seq_len * d->block_size >= ((int64_t)1 << 40)) return ATTN_ERR_SHAPE;

@@ -178,20 +178,28 @@ __device__ __forceinline__ void prefill_wg(const PrefillParams& p, const uint32_
     const int j = bx % p.num_heads;
     hq_grid = p.num_heads % 8 == 0 ? (j % 8) * (p.num_heads / 8) + j / 8 : j;
   } else {
-    // the grid (q tiles, heads, requests); longest (causal) q tiles first. When num_heads is
-    // a multiple of 8 (not in the prefix pass) the grid is read in its linear order, heads
-    // fastest, with the heads placed on the XCDs as in the scheduled mode above. Written with
-    // selects rather than branches: with an if / else-if / else here the compiler left the
-    // head undefined on the non-remapped path (no copy of the workgroup id y on that edge of
-    // the merged control flow), so heads were garbage there.
+    // the grid. When num_heads is a multiple of 8 (not in the prefix pass) it is (q tiles,
+    // heads, requests), read in its linear order, heads fastest, with the heads placed on the
+    // XCDs as in the scheduled mode above and the longest (causal) q tiles of a request
+    // first. Other head counts launch it as (heads, requests, q tiles), q-tile-major: the
+    // last q tile of every request (the heaviest under a causal mask; empty for short
+    // requests, which return at once) before any earlier one, so that a varlen batch's
+    // longest tiles start first. The prefix pass uses (q tiles, kv heads, key slices).
+    // Written with selects rather than branches: with an if / else-if / else here the
+    // compiler left the head undefined on one path (no copy of the workgroup id y on that
+    // edge of the merged control flow).
     const bool remap = !single && p.num_heads % 8 == 0;
     const uint32_t id = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
     const uint32_t per_req = gridDim.x * (uint32_t)p.num_heads;
     const int local = (int)(id % per_req);
     const int j = local % p.num_heads;
-    r = remap ? p.seq_begin + (int)(id / per_req) : (single ? 0 : p.seq_begin + (int)blockIdx.z);
-    qt = (int)gridDim.x - 1 - (remap ? local / p.num_heads : (int)blockIdx.x);
-    hq_grid = remap ? (j % 8) * (p.num_heads / 8) + j / 8 : (int)blockIdx.y;
+    r = remap ? p.seq_begin + (int)(id / per_req)
+              : (single ? 0 : p.seq_begin + (int)blockIdx.y);
+    qt = remap ? (int)gridDim.x - 1 - local / p.num_heads
+               : (single ? (int)gridDim.x - 1 - (int)blockIdx.x
+                         : (int)gridDim.z - 1 - (int)blockIdx.z);
+    hq_grid = remap ? (j % 8) * (p.num_heads / 8) + j / 8
+                    : (single ? (int)blockIdx.y : (int)blockIdx.x);
   }
   r = __builtin_amdgcn_readfirstlane(r);            // wave-uniform
   qt = __builtin_amdgcn_readfirstlane(qt);
@@ -657,7 +665,10 @@ hipError_t launch_mixed(const PrefillParams& p, const DecodeParams& dp, hipStrea
 
 template <int D, bool CAUSAL, bool WINDOW>
 hipError_t launch(const PrefillParams& p, hipStream_t stream) {
-  dim3 grid((p.max_query_len + kBR - 1) / kBR, p.num_heads, p.num_seqs);
+  const unsigned qtiles = (unsigned)((p.max_query_len + kBR - 1) / kBR);
+  // (q tiles, heads, requests) with the XCD head placement, else q-tile-major (see prefill_wg)
+  dim3 grid = p.num_heads % 8 == 0 ? dim3(qtiles, p.num_heads, p.num_seqs)
+                                   : dim3(p.num_heads, p.num_seqs, qtiles);
   if (p.schedule != nullptr) {       // one workgroup per (schedule slot, q head)
     grid = dim3((unsigned)((int64_t)p.num_seqs * p.max_qtiles * p.num_heads), 1, 1);
   } else if (p.single_ql > 0) {            // prefix pass: (token, head) rows per kv head, key slices

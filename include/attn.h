@@ -146,7 +146,8 @@ attn_status attn_decode_partition_tokens(const attn_desc* desc, int32_t* tokens)
  *                   soon as the kernels are queued.
  *
  * Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE (negative or inconsistent sizes, more than 65535
- * requests or than 65535 decode partitions of max_seq_len), ATTN_ERR_BLOCK_SIZE ([FA] Backend
+ * requests, than 65535 256-row query tiles of max_query_len or than 65535 decode partitions
+ * of max_seq_len), ATTN_ERR_BLOCK_SIZE ([FA] Backend
  * raises on block_size % 16 != 0), ATTN_ERR_GQA, ATTN_ERR_UNSUPPORTED (head_size not 64/128, unknown
  * dtype, partition_tokens not a multiple of 128 in [128, 16384], window > 0 without
  * causal, scale not finite and > 0),

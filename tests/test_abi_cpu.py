@@ -77,6 +77,9 @@ def _fwd(desc, causal=1, window=0, scale=0.125, ws=None, ws_bytes=0, q=FAKE, out
     (dict(num_tokens=-1), A.ATTN_ERR_SHAPE),
     (dict(max_seq_len=49), A.ATTN_ERR_SHAPE),       # exceeds max_blocks_per_seq * block_size
     (dict(max_query_len=41), A.ATTN_ERR_SHAPE),
+    # more than 65535 256-row query tiles (a grid dimension of the prefill kernel)
+    (dict(max_query_len=256 * 65535 + 1, max_seq_len=256 * 65535 + 1,
+          max_blocks_per_seq=(256 * 65535) // 16 + 1), A.ATTN_ERR_SHAPE),
     # more than 65535 decode partitions of max_seq_len (a grid dimension of the split kernel)
     (dict(partition_tokens=128, max_seq_len=128 * 65535 + 1,
           max_blocks_per_seq=(128 * 65535) // 16 + 1), A.ATTN_ERR_SHAPE),
