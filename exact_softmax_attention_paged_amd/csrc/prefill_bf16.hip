@@ -178,28 +178,30 @@ __device__ __forceinline__ void prefill_wg(const PrefillParams& p, const uint32_
     const int j = bx % p.num_heads;
     hq_grid = p.num_heads % 8 == 0 ? (j % 8) * (p.num_heads / 8) + j / 8 : j;
   } else {
-    // the grid. When num_heads is a multiple of 8 (not in the prefix pass) it is (q tiles,
-    // heads, requests), read in its linear order, heads fastest, with the heads placed on the
-    // XCDs as in the scheduled mode above and the longest (causal) q tiles of a request
-    // first. Other head counts launch it as (heads, requests, q tiles), q-tile-major: the
+    // the grid. Head size 128 with num_heads a multiple of 8 (not in the prefix pass): (q
+    // tiles, heads, requests), read in its linear order, heads fastest, each request's
+    // longest (causal) q tiles first. Otherwise (heads, requests, q tiles), q-tile-major: the
     // last q tile of every request (the heaviest under a causal mask; empty for short
-    // requests, which return at once) before any earlier one, so that a varlen batch's
-    // longest tiles start first. The prefix pass uses (q tiles, kv heads, key slices).
-    // Written with selects rather than branches: with an if / else-if / else here the
-    // compiler left the head undefined on one path (no copy of the workgroup id y on that
-    // edge of the merged control flow).
+    // requests, which return at once) before any earlier one. Head size 64 fits two
+    // workgroups on a CU, and the q-tile-major order pairs heavy and light tiles on the CUs
+    // where the request-major one paired equal ones (a 4 x 1024-token batch, 32 heads: 41.2
+    // -> 32.5 us); for head size 128 (one workgroup per CU) the request-major order was 4 %
+    // faster on the mixed workload's prefill rows. When num_heads is a multiple of 8 the
+    // heads are placed on the XCDs as in the scheduled mode above. The prefix pass uses (q
+    // tiles, kv heads, key slices). Written with selects rather than branches: with an if /
+    // else-if / else here the compiler left the head undefined on one path (no copy of the
+    // workgroup id y on that edge of the merged control flow).
     const bool remap = !single && p.num_heads % 8 == 0;
+    const bool qmajor = !single && (D == 64 || p.num_heads % 8 != 0);
     const uint32_t id = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
     const uint32_t per_req = gridDim.x * (uint32_t)p.num_heads;
     const int local = (int)(id % per_req);
-    const int j = local % p.num_heads;
-    r = remap ? p.seq_begin + (int)(id / per_req)
-              : (single ? 0 : p.seq_begin + (int)blockIdx.y);
-    qt = remap ? (int)gridDim.x - 1 - local / p.num_heads
-               : (single ? (int)gridDim.x - 1 - (int)blockIdx.x
-                         : (int)gridDim.z - 1 - (int)blockIdx.z);
-    hq_grid = remap ? (j % 8) * (p.num_heads / 8) + j / 8
-                    : (single ? (int)blockIdx.y : (int)blockIdx.x);
+    const int j = qmajor ? (int)blockIdx.x : local % p.num_heads;
+    r = single ? 0 : p.seq_begin + (qmajor ? (int)blockIdx.y : (int)(id / per_req));
+    qt = single ? (int)gridDim.x - 1 - (int)blockIdx.x
+                : (qmajor ? (int)gridDim.z - 1 - (int)blockIdx.z
+                          : (int)gridDim.x - 1 - local / p.num_heads);
+    hq_grid = single ? (int)blockIdx.y : (remap ? (j % 8) * (p.num_heads / 8) + j / 8 : j);
   }
   r = __builtin_amdgcn_readfirstlane(r);            // wave-uniform
   qt = __builtin_amdgcn_readfirstlane(qt);
@@ -666,9 +668,10 @@ hipError_t launch_mixed(const PrefillParams& p, const DecodeParams& dp, hipStrea
 template <int D, bool CAUSAL, bool WINDOW>
 hipError_t launch(const PrefillParams& p, hipStream_t stream) {
   const unsigned qtiles = (unsigned)((p.max_query_len + kBR - 1) / kBR);
-  // (q tiles, heads, requests) with the XCD head placement, else q-tile-major (see prefill_wg)
-  dim3 grid = p.num_heads % 8 == 0 ? dim3(qtiles, p.num_heads, p.num_seqs)
-                                   : dim3(p.num_heads, p.num_seqs, qtiles);
+  // (q tiles, heads, requests), request-major, or (heads, requests, q tiles), q-tile-major
+  // (the orders are explained in prefill_wg)
+  dim3 grid = D == 128 && p.num_heads % 8 == 0 ? dim3(qtiles, p.num_heads, p.num_seqs)
+                                               : dim3(p.num_heads, p.num_seqs, qtiles);
   if (p.schedule != nullptr) {       // one workgroup per (schedule slot, q head)
     grid = dim3((unsigned)((int64_t)p.num_seqs * p.max_qtiles * p.num_heads), 1, 1);
   } else if (p.single_ql > 0) {            // prefix pass: (token, head) rows per kv head, key slices
