@@ -583,6 +583,8 @@ def probes():
         L.attn_probe_read_stream.restype = i32
         L.attn_probe_mfma_loop.argtypes = [vp, vp, i32, i32, vp]
         L.attn_probe_mfma_loop.restype = i32
+        L.attn_probe_lds_read.argtypes = [vp, vp, i32, i32, i32, vp]
+        L.attn_probe_lds_read.restype = i32
         _probes = L
     return _probes
 
@@ -605,6 +607,26 @@ def mfma_probe(dev, workgroups=256, iters=20000, reps=3):
     return flops / (ms / 1e3) / 1e12, mhz
 
 
+def lds_probe(dev, transposing, workgroups=256, iters=4000, reps=3):
+    """Run the LDS read probe: returns (bytes per shader clock per CU, shader clock in MHz,
+    TB/s over the whole chip)."""
+    import ctypes
+    import torch
+    clocks = torch.zeros(4 * workgroups, dtype=torch.int64, device=dev)
+    sink = torch.zeros(512 * workgroups, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def run():
+        assert probes().attn_probe_lds_read(clocks.data_ptr(), sink.data_ptr(), workgroups,
+                                            iters, int(transposing), stream) == 0
+    ms = _time_ms(run, reps, warmup=1)
+    c = clocks.view(workgroups, 4).cpu().numpy().astype(np.float64)
+    cycles = float(np.median(c[:, 1] - c[:, 0]))
+    mhz = float(np.median((c[:, 1] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 2], 1.0) * 100.0))
+    per_wg = 8.0 * iters * 8 * (512 if transposing else 1024)
+    return per_wg / cycles, mhz, workgroups * per_wg / (ms / 1e3) / 1e12
+
+
 def ceilings_report(dev):
     """What this device delivers outside the attention kernels, beside the spec peaks the
     roofline fractions use. Own probes (libattn_probes.so, the instruction forms the kernels
@@ -613,7 +635,9 @@ def ceilings_report(dev):
     v_mfma_f32_32x32x16_bf16 (8 waves per workgroup, 4 independent accumulators per wave) with
     the shader clock under that load. Vendor paths beside them: a bf16 GEMM through torch.mm
     (8192 x 8192 x 8192, contiguous operands) and a 4 GiB device-to-device copy (read + write
-    bytes). One JSON line each."""
+    bytes). Last, the LDS read rate per CU of the prefill kernel's two LDS read forms
+    (ds_read_b128 for its K operands, ds_read_b64_tr_b16 for its V^T operands; one workgroup of
+    8 waves per CU, 8 reads in flight per wave). One JSON line each."""
     import ctypes
     import torch
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
@@ -659,6 +683,14 @@ def ceilings_report(dev):
                       "ms": round(ms, 4), "gbps": round(byts / (ms / 1e3) / 1e9, 1),
                       "frac_of_spec": round(byts / (ms / 1e3) / PEAK_HBM_BYTES, 4)}),
           flush=True)
+    del src, dst
+    for tr in (0, 1):
+        bpc, mhz, tbps = lds_probe(dev, tr)
+        print(json.dumps({"report": "ceilings", "what": "own LDS read loop, 256 workgroups x 8 "
+                          "waves, " + ("ds_read_b64_tr_b16 (8 bytes per lane)" if tr else
+                                       "ds_read_b128 (16 bytes per lane)"),
+                          "bytes_per_clock_per_cu": round(bpc, 1), "shader_clock_mhz": round(mhz, 1),
+                          "tbps_chip": round(tbps, 1)}), flush=True)
 
 
 def mixed_step(batch, layers, dev):

@@ -8,7 +8,8 @@
  * delivers for the two operations the kernels are bound by, with the instruction forms the
  * kernels use: 16-byte global loads streaming from HBM (what the split-KV decode kernel does
  * with the paged K/V rows) and back-to-back v_mfma_f32_32x32x16_bf16 (the prefill kernel's QK^T
- * and PV products), plus the shader clock under that MFMA load.
+ * and PV products), plus the shader clock under that MFMA load, and the LDS read rate of the
+ * prefill kernel's two LDS read forms (its K and V^T operand reads).
  *
  * Conventions: device pointers are caller-owned; kernels are queued on `stream` (a hipStream_t,
  * NULL = the null stream) and the call returns once they are queued. Return value: 0 on success,
@@ -48,6 +49,18 @@ int32_t attn_probe_read_stream(const void* src, uint64_t bytes, uint32_t* sink,
  */
 int32_t attn_probe_mfma_loop(uint64_t* clocks, float* sink, int32_t workgroups, int32_t iters,
                              void* stream);
+
+/*
+ * attn_probe_lds_read: `workgroups` workgroups of 8 waves, each with a 64 KiB LDS tile filled
+ * once; every wave then issues `iters` rounds of 8 independent LDS reads and folds what it reads
+ * into one uint32 per thread, written to sink[workgroups * 512]. transposing == 0:
+ * ds_read_b128 (16 bytes per lane, 1 KiB per read); transposing != 0: ds_read_b64_tr_b16
+ * (8 bytes per lane, 512 bytes per read) with the prefill kernel's V^T addressing for
+ * head_size 128. Bytes read per workgroup: 8 * iters * 8 * (1024 or 512). clocks as for
+ * attn_probe_mfma_loop (wave 0: start and end shader clock, start and end 100 MHz reference).
+ */
+int32_t attn_probe_lds_read(uint64_t* clocks, uint32_t* sink, int32_t workgroups, int32_t iters,
+                            int32_t transposing, void* stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ def test_header_declares_the_python_names():
 def test_probe_library_exports_its_header():
     src = open(os.path.join(ROOT, "include", "attn_probes.h")).read()
     declared = sorted(set(re.findall(r"^\S[^\n(]*?\b(attn_probe_[a-z0-9_]+)\s*\(", src, re.M)))
-    assert declared == ["attn_probe_mfma_loop", "attn_probe_read_stream"]
+    assert declared == ["attn_probe_lds_read", "attn_probe_mfma_loop", "attn_probe_read_stream"]
     lib = os.path.join(os.path.dirname(A.LIB_PATH), "libattn_probes.so")
     out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True,
                          check=True).stdout
