@@ -13,9 +13,9 @@
 // through two LDS buffers:
 //   * the next tile's K and V rows go from HBM straight into the other buffer
 //     (global_load_lds_dwordx4) while the current tile is consumed: no register staging and
-//     no LDS stores. One wave of each SIMD pair issues them; the other goes straight to its
-//     MFMAs. The block ids of the tile after it are fetched at the same time, so the
-//     addresses are ready when its loads are issued; one barrier per tile;
+//     no LDS stores. Every wave issues its share of them between its QK^T k-chunks. The
+//     block ids of the tile after it are fetched at the same time, so the addresses are
+//     ready when its loads are issued; one barrier per tile;
 //   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, Q^T held in
 //     registers as the B operand). On gfx950 this shape sustains about 1.6x the bf16 rate of
 //     the 16x16x32 shape. Each lane holds 16 keys of one query, so the row max and row sum
